@@ -1,0 +1,187 @@
+"""Plain, slow, obviously correct scaled-dot-product attention on the CPU in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): the product path never calls this.
+
+What is computed is the plain definition of attention, with the full score matrix
+materialised, because the tiled method reaches exactly the same result in real arithmetic:
+the FlashAttention-T commentary (ai-stack.site, "FlashAttention-T：张量化注意力机制优化方案",
+learning points) states the tiled algorithm keeps numerically the same result as standard
+attention, and the xxqk.cn article ("Attention算子实战：从CUDA优化到昇腾/CANN部署",
+section 2.2) describes it as the same QK^T -> softmax -> PV computed block by block.
+
+Definition followed, per batch b and query head hq, with G = Hq / Hkv and hk = hq // G:
+
+    S[i, j] = scale * sum_k Q[b, hq, i, k] * K[b, hk, j, k]
+    S[i, j] = -inf               where causal and j > i
+    P[i, j] = exp(S[i, j] - max_j S[i, j])
+    O[b, hq, i, :] = sum_j P[i, j] * V[b, hk, j, :] / sum_j P[i, j]
+
+Sources for each step:
+  * max-subtracted exponent, row sum, then the product with V: the "fused attention"
+    example on the FlashAttention-T page (code example 2) and the stable-softmax remark in
+    section 2.2 of the xxqk.cn article;
+  * ``(q * scale) @ k^T -> softmax -> @ v``: the ``raw_attention`` helper of the ewbang.com
+    article (PyTorch FlashAttention for Turing, verification script);
+  * tensor shapes [batch, heads, seq, head_dim], the causal flag and the default scale
+    1/sqrt(head_dim): the API bullets of the jeff.news Aule-Attention article;
+  * heads_q a multiple of heads_kv (grouped-query attention): same bullets, and the GQA /
+    MQA examples of the jdon.com Aule-Attention article. The reading taken is that query
+    head hq uses key/value head hq // G, i.e. K/V expanded with repeat_interleave;
+  * varlen over packed ``qkv[total_tokens, 3, heads, head_dim]`` with cumulative
+    ``cu_seqlens`` (``[0, 5, 12]`` means qkv[0:5] and qkv[5:12]), attention within each
+    sequence only, output ``[total_tokens, heads, head_dim]``: the docstring of the
+    varlen function in the ewbang.com article.
+
+Readings where the pages are silent:
+  * causal masking is top-left (key j is visible to query i iff j <= i) and needs
+    seqlen_q == seqlen_k; the pages only show equal lengths;
+  * the scale is applied to the float64 dot product as the exact float32 value the
+    library receives;
+  * inputs are the values already rounded to the storage dtype (the generators do that);
+    they are upcast exactly to float64 here.
+
+Library primitives used as steps: numpy matmul (the dot products), numpy exp and sums.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def _scale64(scale) -> float:
+    # the library takes the scale as a C float: the oracle uses that exact value
+    return float(np.float32(scale))
+
+
+def _check_dense(q, k, v, causal):
+    if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
+        raise ValueError("q, k, v must be [batch, heads, seq, head_dim]")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if v.shape != k.shape or Bk != B or dk != d:
+        raise ValueError("k and v must be [batch, heads_kv, seqlen_k, head_dim]")
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError("heads_q must be a multiple of heads_kv")
+    if causal and Nq != Nk:
+        raise ValueError("causal attention needs seqlen_q == seqlen_k")
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def _kv_head(hq: int, group: int) -> int:
+    """Key/value head read by query head hq when ``group`` query heads share one."""
+    return hq // group
+
+
+def _causal_masked(rows: np.ndarray, n_keys: int) -> np.ndarray:
+    """Boolean [len(rows), n_keys]: True where key j is in the future of query row i."""
+    return np.arange(n_keys)[None, :] > np.asarray(rows)[:, None]
+
+
+def _softmax_rows_times_v(S: np.ndarray, V: np.ndarray) -> np.ndarray:
+    """Row-wise max-subtracted softmax of S (float64, -inf = masked) times V."""
+    m = S.max(axis=1, keepdims=True)
+    P = np.exp(S - m)
+    l = P.sum(axis=1, keepdims=True)
+    return (P @ V) / l
+
+
+def attention_ref(q, k, v, *, causal: bool, scale: float) -> np.ndarray:
+    """Dense / GQA attention. q: [B,Hq,Nq,d]; k, v: [B,Hkv,Nk,d]. Returns float64
+    [B,Hq,Nq,d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Hkv, Nq, Nk, d = _check_dense(q, k, v, causal)
+    G = Hq // Hkv
+    sc = _scale64(scale)
+    out = np.empty((B, Hq, Nq, d), dtype=np.float64)
+    if causal:
+        masked = _causal_masked(np.arange(Nq), Nk)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = _kv_head(hq, G)
+            S = sc * (q[b, hq] @ k[b, hk].T)
+            if causal:
+                S[masked] = -np.inf
+            out[b, hq] = _softmax_rows_times_v(S, v[b, hk])
+    return out
+
+
+def attention_ref_rows(q, k, v, rows, *, causal: bool, scale: float) -> np.ndarray:
+    """The same attention, for the query rows listed in ``rows`` only (the same rows for
+    every batch and head). Returns float64 [B,Hq,len(rows),d]. Under causal masking row i
+    sees keys 0..i."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Hkv, Nq, Nk, d = _check_dense(q, k, v, causal)
+    rows = np.asarray(rows, dtype=np.int64)
+    if rows.size and (rows.min() < 0 or rows.max() >= Nq):
+        raise ValueError("row index out of range")
+    G = Hq // Hkv
+    sc = _scale64(scale)
+    out = np.empty((B, Hq, rows.size, d), dtype=np.float64)
+    if causal:
+        masked = _causal_masked(rows, Nk)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = _kv_head(hq, G)
+            S = sc * (q[b, hq, rows] @ k[b, hk].T)
+            if causal:
+                S[masked] = -np.inf
+            out[b, hq] = _softmax_rows_times_v(S, v[b, hk])
+    return out
+
+
+def _check_varlen(qkv, cu_seqlens):
+    qkv = _f64(qkv)
+    if qkv.ndim != 4 or qkv.shape[1] != 3:
+        raise ValueError("qkv must be [total_tokens, 3, heads, head_dim]")
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    if cu.ndim != 1 or cu.size < 2 or cu[0] != 0 or np.any(np.diff(cu) < 0):
+        raise ValueError("cu_seqlens must be non-decreasing, start at 0, length batch+1")
+    if cu[-1] != qkv.shape[0]:
+        raise ValueError("cu_seqlens[-1] must equal total_tokens")
+    return qkv, cu
+
+
+def _seq_as_dense(qkv, a, e):
+    # [L, 3, H, d] slice -> three [1, H, L, d] tensors
+    seg = qkv[a:e]
+    return tuple(np.ascontiguousarray(seg[:, c].transpose(1, 0, 2))[None] for c in range(3))
+
+
+def attention_ref_varlen(qkv, cu_seqlens, *, causal: bool, scale: float) -> np.ndarray:
+    """Varlen attention over packed qkv [T,3,H,d]: each sequence cu[s]:cu[s+1] attends
+    only within itself, with causal positions counted from the sequence start.
+    Returns float64 [T,H,d]."""
+    qkv, cu = _check_varlen(qkv, cu_seqlens)
+    T, _, H, d = qkv.shape
+    out = np.empty((T, H, d), dtype=np.float64)
+    for s in range(cu.size - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        if e == a:
+            continue
+        q, k, v = _seq_as_dense(qkv, a, e)
+        out[a:e] = attention_ref(q, k, v, causal=causal, scale=scale)[0].transpose(1, 0, 2)
+    return out
+
+
+def attention_ref_varlen_rows(qkv, cu_seqlens, tokens, *, causal: bool,
+                              scale: float) -> np.ndarray:
+    """Varlen attention for the listed global token indices only. Returns float64
+    [len(tokens),H,d] in the order given."""
+    qkv, cu = _check_varlen(qkv, cu_seqlens)
+    T, _, H, d = qkv.shape
+    tokens = np.asarray(tokens, dtype=np.int64)
+    if tokens.size and (tokens.min() < 0 or tokens.max() >= T):
+        raise ValueError("token index out of range")
+    out = np.empty((tokens.size, H, d), dtype=np.float64)
+    seq_of = np.searchsorted(cu, tokens, side="right") - 1
+    for s in np.unique(seq_of):
+        a, e = int(cu[s]), int(cu[s + 1])
+        sel = np.nonzero(seq_of == s)[0]
+        local = tokens[sel] - a
+        q, k, v = _seq_as_dense(qkv, a, e)
+        res = attention_ref_rows(q, k, v, local, causal=causal, scale=scale)[0]
+        out[sel] = res.transpose(1, 0, 2)
+    return out

@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for the attention forward, shared by the tests and the bench.
+
+This module draws random numbers, rounds them to the storage dtype and describes the
+workload shapes. It contains none of the attention arithmetic: neither the CPU oracle
+nor the HIP path lives here, and it imports neither.
+
+Recipe (the same for every workload):
+  * generator  ``np.random.default_rng(seed)`` (PCG64);
+  * dense:  ``standard_normal(shape, dtype=float32)`` drawn in the order Q, K, V, each
+    multiplied by ``sigma``;
+  * varlen: sequence lengths first (``integers(lo, hi, size=S, endpoint=True)``), then one
+    packed ``qkv`` draw of shape ``[T, 3, H, d]``, multiplied by ``sigma``;
+  * the fp32 draws are rounded to the storage dtype with round-to-nearest-even, and the
+    *rounded* values (held exactly in float32 arrays) are what both the oracle and the GPU
+    see.
+
+The shapes follow the workloads the pages describe: the [batch, heads, seq, head_dim]
+tensors and GQA head counts of the Aule-Attention API examples (jeff.news article
+"AMD GPU에서도 동작하는 FlashAttention 구현체, Aule-Attention", API bullets), the A10
+sequence-2048 / 32-head / head_dim-64 measurement (xxqk.cn article
+"Attention算子实战：从CUDA优化到昇腾/CANN部署", section 2.1) and the packed-QKV varlen
+layout with cu_seqlens (ewbang.com article on a PyTorch FlashAttention for Turing,
+the varlen function's docstring).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+
+
+def round_to_dtype(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 ``x`` to ``dtype`` with round-to-nearest-even; return float32 holding
+    the exactly representable rounded values."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        u = x.view(np.uint32)
+        # RNE on the upper 16 bits: add 0x7FFF plus the lowest kept bit, then truncate.
+        bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+        r = ((u + bias) & np.uint32(0xFFFF0000)).astype(np.uint32)
+        return r.view(np.float32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def dense_inputs(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, *, seed,
+                 sigma=1.0, dtype="bf16"):
+    """Q [B,Hq,Nq,d], K and V [B,Hkv,Nk,d], drawn in that order from one generator."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((batch, heads_q, seqlen_q, head_dim), dtype=np.float32)
+    k = rng.standard_normal((batch, heads_kv, seqlen_k, head_dim), dtype=np.float32)
+    v = rng.standard_normal((batch, heads_kv, seqlen_k, head_dim), dtype=np.float32)
+    if sigma != 1.0:
+        s = np.float32(sigma)
+        q *= s
+        k *= s
+        v *= s
+    return round_to_dtype(q, dtype), round_to_dtype(k, dtype), round_to_dtype(v, dtype)
+
+
+def varlen_lengths(num_seqs, lo, hi, *, seed):
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi, size=num_seqs, endpoint=True), rng
+
+
+def cu_seqlens_from_lengths(lengths) -> np.ndarray:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    np.cumsum(lengths, out=cu[1:])
+    return cu.astype(np.int32)
+
+
+def varlen_inputs(lengths, heads, head_dim, *, seed=None, rng=None, sigma=1.0, dtype="bf16"):
+    """Packed ``qkv [T,3,H,d]`` and int32 ``cu_seqlens [S+1]`` for the given lengths.
+
+    Pass ``rng`` to continue a generator that already drew the lengths."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    cu = cu_seqlens_from_lengths(lengths)
+    total = int(cu[-1])
+    qkv = rng.standard_normal((total, 3, heads, head_dim), dtype=np.float32)
+    if sigma != 1.0:
+        qkv *= np.float32(sigma)
+    return round_to_dtype(qkv, dtype), cu
+
+
+def sampled_rows(seqlen: int, *, seed=1004, n_random=49) -> np.ndarray:
+    """Query rows checked at the long-context size: tile edges plus seeded random rows."""
+    fixed = [0, 1, 2, 63, 64, 127, 128, 255, 256, 4095, 4096, 16383, 16384,
+             seqlen - 2, seqlen - 1]
+    fixed = sorted({r for r in fixed if 0 <= r < seqlen})
+    rng = np.random.default_rng(seed)
+    extra = []
+    taken = set(fixed)
+    while len(extra) < n_random and len(taken) < seqlen:
+        for r in rng.choice(seqlen, n_random, replace=False).tolist():
+            if r not in taken and len(extra) < n_random:
+                taken.add(r)
+                extra.append(r)
+    return np.array(sorted(fixed + extra), dtype=np.int64)
+
+
+@dataclass(frozen=True)
+class DenseConfig:
+    name: str
+    dtype: str
+    batch: int
+    heads_q: int
+    heads_kv: int
+    seqlen: int
+    head_dim: int
+    causal: bool
+    seed: int
+    sigma: float = 1.0
+    scale: float | None = None
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+
+    def pairs(self) -> int:
+        n = self.seqlen
+        per = n * (n + 1) // 2 if self.causal else n * n
+        return self.batch * per
+
+    def flops(self) -> int:
+        """4*d FLOP per unmasked (query, key) pair per q head: QK^T and PV, 2 FLOP/MAC."""
+        return 4 * self.head_dim * self.heads_q * self.pairs()
+
+    def bytes_compulsory(self) -> int:
+        e = {"f32": 4, "f16": 2, "bf16": 2}[self.dtype]
+        n, d = self.seqlen, self.head_dim
+        return e * d * n * self.batch * (2 * self.heads_q + 2 * self.heads_kv)
+
+    def inputs(self):
+        return dense_inputs(self.batch, self.heads_q, self.heads_kv, self.seqlen, self.seqlen,
+                            self.head_dim, seed=self.seed, sigma=self.sigma, dtype=self.dtype)
+
+
+@dataclass(frozen=True)
+class VarlenConfig:
+    name: str
+    dtype: str
+    num_seqs: int
+    len_lo: int
+    len_hi: int
+    heads: int
+    head_dim: int
+    causal: bool
+    seed: int
+    sigma: float = 1.0
+    scale: float | None = None
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+
+    def lengths(self):
+        return varlen_lengths(self.num_seqs, self.len_lo, self.len_hi, seed=self.seed)[0]
+
+    def pairs(self) -> int:
+        L = [int(x) for x in self.lengths()]
+        return sum(l * (l + 1) // 2 if self.causal else l * l for l in L)
+
+    def flops(self) -> int:
+        return 4 * self.head_dim * self.heads * self.pairs()
+
+    def bytes_compulsory(self) -> int:
+        e = {"f32": 4, "f16": 2, "bf16": 2}[self.dtype]
+        total = int(sum(int(x) for x in self.lengths()))
+        return e * total * self.heads * self.head_dim * 4   # q, k, v read + o written
+
+    def inputs(self):
+        lengths, rng = varlen_lengths(self.num_seqs, self.len_lo, self.len_hi, seed=self.seed)
+        qkv, cu = varlen_inputs(lengths, self.heads, self.head_dim, rng=rng, sigma=self.sigma,
+                                dtype=self.dtype)
+        return qkv, cu
+
+
+# The five workloads: a small fp32 case, the A10-shaped fp16 causal case, the bf16 causal
+# GQA case the throughput is quoted on, packed varlen, and a 32k long-context GQA case.
+CONFIGS = {
+    "c1_f32_dense": DenseConfig("c1_f32_dense", "f32", 1, 2, 2, 128, 64, False, seed=0,
+                                scale=0.125),
+    "c2_f16_causal": DenseConfig("c2_f16_causal", "f16", 1, 32, 32, 2048, 64, True, seed=1),
+    "c3_bf16_causal_gqa": DenseConfig("c3_bf16_causal_gqa", "bf16", 4, 32, 8, 4096, 128, True,
+                                      seed=2),
+    "c4_bf16_varlen": VarlenConfig("c4_bf16_varlen", "bf16", 16, 64, 4096, 16, 128, True,
+                                   seed=3),
+    "c5_bf16_long_gqa": DenseConfig("c5_bf16_long_gqa", "bf16", 1, 32, 8, 32768, 128, True,
+                                    seed=4, sigma=0.5),
+}
+
+# Lengths the varlen workload must draw (regenerated and asserted in the tests).
+C4_LENGTHS = [3336, 409, 787, 1019, 795, 3295, 3569, 2411, 222, 443, 1403, 1810, 2569, 1996,
+              1131, 708]
