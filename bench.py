@@ -1,0 +1,202 @@
+"""Throughput of the tiled attention forward on one MI355X.
+
+One step = one aule_attn_fwd call over the whole bf16 causal GQA batch (B=4, Hq=32, Hkv=8,
+N=4096, head_dim=128, scale 1/sqrt(128), seeded N(0,1) inputs) — the full hot path of this
+library on its headline workload. Inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout. `value` is causal-adjusted TFLOP/s (exact count of unmasked
+query-key pairs, 4*d FLOP per pair per query head). The `roofline` object reports the
+attention kernel's achieved rate (HIP events on the launch stream over the timed region)
+against the MI355X dense bf16 MFMA peak; `cpu_baseline` times the CPU fp64 oracle on a
+bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense, published
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c3_bf16_causal_gqa")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget of the oracle sample")
+    ap.add_argument("--all", action="store_true",
+                    help="also time every workload and report them on stderr")
+    return ap.parse_args()
+
+
+def device_inputs(cfg, torch):
+    from workloads import DenseConfig
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    if isinstance(cfg, DenseConfig):
+        q, k, v = cfg.inputs()
+        t = lambda x: torch.from_numpy(x).to(device="cuda", dtype=tdt)
+        return (t(q), t(k), t(v)), (q, k, v)
+    qkv, cu = cfg.inputs()
+    return (torch.from_numpy(qkv).to(device="cuda", dtype=tdt),
+            torch.from_numpy(cu).to("cuda")), (qkv, cu)
+
+
+def make_step(cfg, dev_inputs, torch):
+    import tiled_attention_02_amd as aule
+    from workloads import DenseConfig
+    if isinstance(cfg, DenseConfig):
+        q, k, v = dev_inputs
+        out = torch.empty_like(q)
+        return lambda: aule.flash_attention(q, k, v, causal=cfg.causal, scale=cfg.softmax_scale,
+                                            out=out)
+    qkv, cu = dev_inputs
+    T, _, H, d = qkv.shape
+    out = torch.empty((T, H, d), dtype=qkv.dtype, device=qkv.device)
+    max_len = int(max(cfg.lengths()))
+    return lambda: aule.flash_attn_varlen_qkvpacked_func(qkv, cu, max_len,
+                                                         softmax_scale=cfg.softmax_scale,
+                                                         causal=cfg.causal, out=out)
+
+
+def time_steps(step, steps, warmup, torch):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()          # the stream the kernels are launched on
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / steps, ev0.elapsed_time(ev1) / 1e3 / steps
+
+
+def cpu_baseline(cfg, host_inputs, budget_s):
+    """The CPU fp64 oracle on whole (batch, query head) slices of the workload, as many as
+    fit in about budget_s seconds; scaled to TFLOP/s with the same FLOP count."""
+    import numpy as np
+    import oracle
+    from workloads import DenseConfig
+    threads = len(os.sched_getaffinity(0))
+    if not isinstance(cfg, DenseConfig):
+        qkv, cu = host_inputs
+        t0 = time.perf_counter()
+        done_flops, seqs = 0, 0
+        for s in range(len(cu) - 1):
+            a, e = int(cu[s]), int(cu[s + 1])
+            sub_cu = np.array([0, e - a], dtype=np.int32)
+            oracle.attention_ref_varlen(qkv[a:e], sub_cu, causal=cfg.causal, scale=cfg.softmax_scale)
+            L = e - a
+            done_flops += 4 * cfg.head_dim * cfg.heads * (L * (L + 1) // 2 if cfg.causal else L * L)
+            seqs += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": done_flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+                "kind": "oracle", "sample": f"{seqs} of {len(cu) - 1} sequences, all heads, "
+                f"{dt:.1f} s"}
+    q, k, v = host_inputs
+    G = cfg.heads_q // cfg.heads_kv
+    n = cfg.seqlen
+    pairs = n * (n + 1) // 2 if cfg.causal else n * n
+    t0 = time.perf_counter()
+    heads = 0
+    for b in range(cfg.batch):
+        for hq in range(cfg.heads_q):
+            hk = hq // G
+            oracle.attention_ref(q[b:b + 1, hq:hq + 1], k[b:b + 1, hk:hk + 1], v[b:b + 1, hk:hk + 1],
+                                 causal=cfg.causal, scale=cfg.softmax_scale)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        else:
+            continue
+        break
+    dt = time.perf_counter() - t0
+    flops = 4 * cfg.head_dim * pairs * heads
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {cfg.batch * cfg.heads_q} (batch, query head) slices in full, "
+            f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from workloads import CONFIGS
+
+    cfg = CONFIGS[args.workload]
+    dev_in, host_in = device_inputs(cfg, torch)
+    step = make_step(cfg, dev_in, torch)
+    wall_s, kern_s = time_steps(step, args.steps, args.warmup, torch)
+
+    flops = cfg.flops()
+    value = flops / wall_s / 1e12
+    achieved = flops / kern_s / 1e12
+    peak = MFMA_PEAK_TFLOPS[cfg.dtype]
+    line = {
+        "metric": "attention fwd TFLOPS (causal-adjusted) and % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) inputs)",
+        "config": {"workload": cfg.name, "desc": describe(cfg), "pct_of_peak": round(100 * value / peak, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel_ms": round(kern_s * 1e3, 4),
+                     "algorithmic_flops_per_launch": flops,
+                     "algorithmic_bytes_per_launch": cfg.bytes_compulsory()},
+    }
+    if args.all:
+        for name, c in CONFIGS.items():
+            if name == cfg.name:
+                continue
+            di, _ = device_inputs(c, torch)
+            w, kt = time_steps(make_step(c, di, torch), max(5, args.steps // 5), 3, torch)
+            pk = MFMA_PEAK_TFLOPS[c.dtype]
+            print(f"[bench] {name}: {kt * 1e3:.4f} ms/launch, {c.flops() / kt / 1e12:.1f} TFLOP/s "
+                  f"({100 * c.flops() / kt / 1e12 / pk:.1f}% of {pk:.0f}), "
+                  f"{c.bytes_compulsory() / kt / 1e9:.0f} GB/s compulsory", file=sys.stderr)
+            del di
+            torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(cfg, host_in, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def describe(cfg):
+    from workloads import DenseConfig
+    if isinstance(cfg, DenseConfig):
+        return (f"{cfg.dtype} {'causal' if cfg.causal else 'non-causal'} B={cfg.batch} Hq={cfg.heads_q} "
+                f"Hkv={cfg.heads_kv} N={cfg.seqlen} d={cfg.head_dim} scale={cfg.softmax_scale:.6g}")
+    return (f"{cfg.dtype} varlen {'causal' if cfg.causal else 'non-causal'} {cfg.num_seqs} seqs "
+            f"L~U[{cfg.len_lo},{cfg.len_hi}] H={cfg.heads} d={cfg.head_dim}")
+
+
+if __name__ == "__main__":
+    main()

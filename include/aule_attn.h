@@ -1,0 +1,116 @@
+/*
+ * aule_attn — tiled scaled-dot-product attention forward for AMD Instinct MI355X (gfx950).
+ *
+ * Computes  O = softmax(scale * Q K^T + causal mask) V  without materialising the
+ * [seqlen_q x seqlen_k] score matrix: K/V are streamed tile by tile and the softmax is kept
+ * online as a running row max and row sum. This is the FlashAttention forward described in
+ * the xxqk.cn article "Attention算子实战：从CUDA优化到昇腾/CANN部署" (section 2.2: Q split
+ * into BLOCK_M tiles, K/V into BLOCK_N tiles, stable softmax with max subtraction kept in
+ * registers, partial results multiplied into V and accumulated, only O written back) and in
+ * the online-softmax practice of the FlashAttention-T commentary (ai-stack.site,
+ * "FlashAttention-T：张量化注意力机制优化方案", best practices 4 and 5: running max_score and
+ * sum_exp, fp32 reductions, fp16/bf16 matrix products).
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers, owned by the caller. The library allocates
+ *     nothing, keeps no state between calls and is reentrant. O must not overlap an input.
+ *   - Every call is asynchronous on `stream` (0 = the null stream). The library never
+ *     synchronises and never reads device memory on the host (cu_seqlens included).
+ *   - On any error a status other than AULE_OK is returned synchronously and no kernel is
+ *     launched; aule_last_error() then describes the failure for the calling thread.
+ *   - Tensor data pointers must be 16-byte aligned (the kernels use 128-bit accesses).
+ *   - dtype selects the element type of Q, K, V and O alike: fp32, fp16 or bf16. Products
+ *     and softmax statistics are accumulated in fp32; O is rounded to dtype
+ *     round-to-nearest-even.
+ */
+#ifndef AULE_ATTN_H
+#define AULE_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h> /* hipStream_t */
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    AULE_DTYPE_F32 = 0,
+    AULE_DTYPE_F16 = 1,
+    AULE_DTYPE_BF16 = 2
+} aule_dtype_t;
+
+typedef enum {
+    AULE_OK = 0,
+    AULE_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned or overlapping buffer, non-finite scale */
+    AULE_ERR_UNSUPPORTED = 2,      /* head_dim > 128 or not a multiple of 8, causal with seqlen_q != seqlen_k, unknown dtype */
+    AULE_ERR_HIP = 3               /* the HIP runtime reported an error at launch */
+} aule_status_t;
+
+/*
+ * Dense / grouped-query attention forward.
+ *
+ * Operation: the [batch, heads, seq_len, head_dim] attention of the Aule-Attention API
+ * (jeff.news article "AMD GPU에서도 동작하는 FlashAttention 구현체, Aule-Attention", API
+ * bullets): fp16/bf16/fp32, head_dim up to 128, heads_q a multiple of heads_kv. Query head
+ * hq reads key/value head hq / (heads_q / heads_kv) — K/V repeated in place, as in the GQA
+ * (32 query / 8 kv heads) and MQA (one kv head) examples of the jdon.com Aule-Attention
+ * article.
+ *
+ *   q : [batch, heads_q,  seqlen_q, head_dim]  contiguous, dtype
+ *   k : [batch, heads_kv, seqlen_k, head_dim]  contiguous, dtype
+ *   v : [batch, heads_kv, seqlen_k, head_dim]  contiguous, dtype
+ *   o : [batch, heads_q,  seqlen_q, head_dim]  contiguous, dtype (written)
+ *   causal : nonzero masks key j for query i when j > i (needs seqlen_q == seqlen_k)
+ *   scale  : multiplies Q K^T before the softmax; any finite value (1/sqrt(head_dim) is
+ *            the usual choice, 0 gives the mean of the visible V rows)
+ *
+ * batch == 0 or seqlen_q == 0 is an empty problem: AULE_OK, nothing launched, pointers not
+ * inspected. Otherwise heads_q, heads_kv, seqlen_k >= 1 and heads_q % heads_kv == 0
+ * (AULE_ERR_INVALID_ARGUMENT); 8 <= head_dim <= 128 with head_dim % 8 == 0
+ * (AULE_ERR_UNSUPPORTED below or above that).
+ */
+aule_status_t aule_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv,
+                            int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                            int32_t causal, float scale, aule_dtype_t dtype,
+                            hipStream_t stream);
+
+/*
+ * Variable-length attention forward over packed QKV.
+ *
+ * Operation: flash_attn_varlen_qkvpacked_func as documented in the ewbang.com article on a
+ * PyTorch FlashAttention for Turing (docstring of the varlen function): packed
+ * qkv [total_tokens, 3, heads, head_dim]; cu_seqlens [num_seqs + 1] cumulative lengths
+ * ([0, 5, 12] = two sequences, qkv[0:5] and qkv[5:12]); each sequence attends only within
+ * itself; causal positions count from the sequence start; output [total_tokens, heads,
+ * head_dim].
+ *
+ *   qkv        : [total_tokens, 3, heads, head_dim] contiguous, dtype
+ *   cu_seqlens : [num_seqs + 1] int32, DEVICE memory, cu[0] = 0, non-decreasing,
+ *                cu[num_seqs] = total_tokens. Not read on the host; a violating array is
+ *                undefined behaviour of the caller, but the kernels clamp every index to
+ *                [0, total_tokens) so it cannot make them read or write out of bounds.
+ *   o          : [total_tokens, heads, head_dim] contiguous, dtype (written)
+ *   max_seqlen : the caller's bound on the longest sequence (a hint; must be >= 0)
+ *
+ * total_tokens == 0 is an empty problem: AULE_OK, nothing launched. Otherwise num_seqs >= 1,
+ * heads >= 1, and the head_dim / dtype / scale rules of aule_attn_fwd apply.
+ */
+aule_status_t aule_attn_fwd_varlen(const void* qkv, const int32_t* cu_seqlens, void* o,
+                                   int32_t num_seqs, int32_t total_tokens,
+                                   int32_t max_seqlen, int32_t heads, int32_t head_dim,
+                                   int32_t causal, float scale, aule_dtype_t dtype,
+                                   hipStream_t stream);
+
+/* Static, NUL-terminated name of a status code. Never NULL. */
+const char* aule_status_string(aule_status_t status);
+
+/* Text describing the most recent failing call made by the calling thread ("" if none).
+ * Valid until the next call into the library from this thread. */
+const char* aule_last_error(void);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* AULE_ATTN_H */

@@ -1,0 +1,143 @@
+"""C-ABI contract tests that need no GPU: the library loads, exports every function the
+header declares, and rejects every invalid argument with the documented status before
+any HIP call (so no device is touched). Fake, never-dereferenced pointer values are used
+where a pointer must be non-null."""
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_attention_02_amd as aule
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "aule_attn.h")
+
+F32, F16, BF16 = aule.AULE_DTYPE_F32, aule.AULE_DTYPE_F16, aule.AULE_DTYPE_BF16
+OK, INV, UNS = aule.AULE_OK, aule.AULE_ERR_INVALID_ARGUMENT, aule.AULE_ERR_UNSUPPORTED
+
+# distinct, 16-byte aligned, never dereferenced: each call below fails validation first
+P = {"q": 0x10000000, "k": 0x20000000, "v": 0x30000000, "o": 0x40000000,
+     "qkv": 0x50000000, "cu": 0x60000000}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(aule.LIB_PATH):
+        from tiled_attention_02_amd.build import build
+        build()
+    return aule.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(aule_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert set(names) == set(aule.EXPORTED), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", aule.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (aule_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings(lib):
+    assert aule.aule_status_string(OK) == "AULE_OK"
+    assert aule.aule_status_string(INV) == "AULE_ERR_INVALID_ARGUMENT"
+    assert aule.aule_status_string(UNS) == "AULE_ERR_UNSUPPORTED"
+    assert aule.aule_status_string(aule.AULE_ERR_HIP) == "AULE_ERR_HIP"
+    assert aule.aule_status_string(99) == "AULE_STATUS_UNKNOWN"
+
+
+def fwd(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], o=P["o"], batch=1, heads_q=4, heads_kv=2,
+             seqlen_q=16, seqlen_k=16, head_dim=64, causal=1, scale=0.125, dtype=BF16,
+             stream=None)
+    a.update(kw)
+    return aule.aule_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["batch"], a["heads_q"],
+                              a["heads_kv"], a["seqlen_q"], a["seqlen_k"], a["head_dim"],
+                              a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+def varlen(**kw):
+    a = dict(qkv=P["qkv"], cu=P["cu"], o=P["o"], num_seqs=2, total_tokens=12, max_seqlen=7,
+             heads=2, head_dim=64, causal=1, scale=0.125, dtype=F16, stream=None)
+    a.update(kw)
+    return aule.aule_attn_fwd_varlen(a["qkv"], a["cu"], a["o"], a["num_seqs"],
+                                     a["total_tokens"], a["max_seqlen"], a["heads"],
+                                     a["head_dim"], a["causal"], a["scale"], a["dtype"],
+                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INV), (dict(k=None), INV), (dict(v=None), INV), (dict(o=None), INV),
+    (dict(batch=-1), INV), (dict(seqlen_q=-3), INV),
+    (dict(heads_q=0), INV), (dict(heads_kv=0), INV), (dict(heads_q=6, heads_kv=4), INV),
+    (dict(seqlen_k=0, causal=0), INV),
+    (dict(head_dim=0), INV), (dict(head_dim=-8), INV),
+    (dict(head_dim=136), UNS), (dict(head_dim=256), UNS), (dict(head_dim=60), UNS),
+    (dict(head_dim=4), UNS),
+    (dict(seqlen_q=16, seqlen_k=32, causal=1), UNS),
+    (dict(scale=math.inf), INV), (dict(scale=math.nan), INV), (dict(scale=-math.inf), INV),
+    (dict(dtype=7), UNS), (dict(dtype=-1), UNS),
+    (dict(q=P["q"] + 8), INV), (dict(o=P["o"] + 2), INV),
+    (dict(o=P["q"]), INV), (dict(o=P["k"] + 64), INV),
+])
+def test_fwd_rejects_invalid_arguments(lib, kw, status):
+    assert fwd(**kw) == status
+    assert aule.aule_last_error() != ""
+
+
+def test_fwd_empty_problems_are_noops(lib):
+    # nothing is launched: null pointers are fine for an empty problem
+    assert fwd(batch=0, q=None, k=None, v=None, o=None) == OK
+    assert fwd(seqlen_q=0, seqlen_k=0, q=None, k=None, v=None, o=None) == OK
+    assert aule.aule_last_error() == ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qkv=None), INV), (dict(cu=None), INV), (dict(o=None), INV),
+    (dict(num_seqs=0), INV), (dict(num_seqs=-2), INV), (dict(total_tokens=-1), INV),
+    (dict(max_seqlen=-1), INV), (dict(heads=0), INV),
+    (dict(head_dim=200), UNS), (dict(head_dim=12), UNS), (dict(dtype=3), UNS),
+    (dict(scale=math.nan), INV),
+    (dict(qkv=P["qkv"] + 4), INV), (dict(cu=P["cu"] + 2), INV),
+    (dict(o=P["qkv"] + 1024), INV),
+])
+def test_varlen_rejects_invalid_arguments(lib, kw, status):
+    assert varlen(**kw) == status
+    assert aule.aule_last_error() != ""
+
+
+def test_varlen_empty_problem_is_noop(lib):
+    assert varlen(total_tokens=0, qkv=None, cu=None, o=None) == OK
+
+
+def test_python_wrappers_refuse_cpu_tensors(lib):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        aule.flash_attention(q, q, q)
+    qkv = torch.zeros(8, 3, 2, 64, dtype=torch.float16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        aule.flash_attn_varlen_qkvpacked_func(qkv, cu, 8)
+    for kw in (dict(dropout_p=0.1), dict(window_size=(4, 4)), dict(softcap=1.0),
+               dict(alibi_slopes=torch.zeros(2)), dict(return_attn_probs=True)):
+        with pytest.raises(NotImplementedError):
+            aule.flash_attn_varlen_qkvpacked_func(qkv, cu, 8, **kw)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(aule, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        aule.load_library(str(tmp_path / "absent.so"))

@@ -1,0 +1,294 @@
+"""GPU parity: the HIP path (through the C-ABI library) against the CPU fp64 oracle on the
+same seeded, dtype-rounded inputs.
+
+Bars (max abs error over every compared element, outputs of O(1) magnitude): 1e-5 for
+fp32, 2e-3 for fp16, 1e-2 for bf16. Small shapes are compared in full; the full-size
+workloads are compared on sampled query rows the oracle computes one by one, plus
+properties that hold at any size.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import tiled_attention_02_amd as aule
+from workloads import (CONFIGS, cu_seqlens_from_lengths, dense_inputs, sampled_rows,
+                       varlen_inputs)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
+TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    aule.load_library()
+
+
+def dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=TDT[dtype])
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def run_dense(q, k, v, dtype, causal, scale):
+    o = aule.flash_attention(dev(q, dtype), dev(k, dtype), dev(v, dtype), causal=causal,
+                             scale=scale)
+    torch.cuda.synchronize()
+    return host(o)
+
+
+def tolerance(dtype, scale, d):
+    """The stated bars hold for scores of the standard magnitude (scale = 1/sqrt(d)). The
+    fp32 error comes from rounding in the fp32 dot products, which grows with |scale|*sqrt(d)
+    (the score magnitude), so for larger scales the fp32 bar is scaled by that ratio."""
+    if dtype == "f32":
+        return TOL[dtype] * max(1.0, abs(scale) * math.sqrt(d))
+    return TOL[dtype]
+
+
+def check_dense(B, Hq, Hkv, Nq, Nk, d, dtype, causal, scale=None, seed=0, sigma=1.0):
+    say(f"dense B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal} "
+        f"scale={scale} seed={seed}")
+    q, k, v = dense_inputs(B, Hq, Hkv, Nq, Nk, d, seed=seed, sigma=sigma, dtype=dtype)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    got = run_dense(q, k, v, dtype, causal, sc)
+    ref = oracle.attention_ref(q, k, v, causal=causal, scale=sc)
+    err = float(np.max(np.abs(got - ref)))
+    assert np.all(np.isfinite(got))
+    tol = tolerance(dtype, sc, d)
+    assert err <= tol, f"max abs err {err} > {tol}"
+    return err
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_c1_f32_dense_full():
+    c = CONFIGS["c1_f32_dense"]
+    q, k, v = c.inputs()
+    got = run_dense(q, k, v, c.dtype, c.causal, c.softmax_scale)
+    ref = oracle.attention_ref(q, k, v, causal=c.causal, scale=c.softmax_scale)
+    assert np.max(np.abs(got - ref)) <= TOL["f32"]
+
+
+def test_c2_f16_causal_full():
+    c = CONFIGS["c2_f16_causal"]
+    q, k, v = c.inputs()
+    got = run_dense(q, k, v, c.dtype, c.causal, c.softmax_scale)
+    ref = oracle.attention_ref(q, k, v, causal=c.causal, scale=c.softmax_scale)
+    err = np.max(np.abs(got - ref))
+    say(f"c2 max abs err {err:.3e}")
+    assert err <= TOL["f16"]
+
+
+def _sampled_dense(name, rows):
+    c = CONFIGS[name]
+    q, k, v = c.inputs()
+    got = run_dense(q, k, v, c.dtype, c.causal, c.softmax_scale)
+    ref = oracle.attention_ref_rows(q, k, v, rows, causal=c.causal, scale=c.softmax_scale)
+    err = np.max(np.abs(got[:, :, rows] - ref))
+    say(f"{name} sampled max abs err {err:.3e} over {rows.size} rows x {q.shape[0] * q.shape[1]} heads")
+    assert np.all(np.isfinite(got))
+    # causal row 0 is V[0] of the head's kv head, at any size
+    G = c.heads_q // c.heads_kv
+    v0 = np.repeat(v[:, :, 0, :], G, axis=1)
+    assert np.max(np.abs(got[:, :, 0, :] - v0)) <= TOL[c.dtype]
+    assert err <= TOL[c.dtype]
+
+
+def test_c3_bf16_causal_gqa_sampled():
+    _sampled_dense("c3_bf16_causal_gqa", sampled_rows(4096))
+
+
+def test_c5_bf16_long_gqa_sampled():
+    _sampled_dense("c5_bf16_long_gqa", sampled_rows(32768))
+
+
+def run_varlen(qkv, cu, dtype, causal, scale, max_seqlen=None):
+    cu_d = torch.from_numpy(cu).to("cuda")
+    if max_seqlen is None:
+        max_seqlen = int(np.max(np.diff(cu))) if cu.size > 1 else 0
+    o = aule.flash_attn_varlen_qkvpacked_func(dev(qkv, dtype), cu_d, max_seqlen,
+                                              softmax_scale=scale, causal=causal)
+    torch.cuda.synchronize()
+    return host(o)
+
+
+def varlen_sample_tokens(cu, seed=5, per_seq=6):
+    rng = np.random.default_rng(seed)
+    toks = []
+    for s in range(cu.size - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        L = e - a
+        if L == 0:
+            continue
+        local = {0, min(1, L - 1), L // 2, max(L - 2, 0), L - 1, min(127, L - 1), min(128, L - 1)}
+        local |= set(rng.integers(0, L, size=per_seq).tolist())
+        toks += [a + x for x in sorted(local)]
+    return np.array(toks, dtype=np.int64)
+
+
+def test_c4_bf16_varlen_sampled():
+    c = CONFIGS["c4_bf16_varlen"]
+    qkv, cu = c.inputs()
+    got = run_varlen(qkv, cu, c.dtype, c.causal, c.softmax_scale)
+    toks = varlen_sample_tokens(cu)
+    ref = oracle.attention_ref_varlen_rows(qkv, cu, toks, causal=c.causal, scale=c.softmax_scale)
+    err = np.max(np.abs(got[toks] - ref))
+    say(f"c4 sampled max abs err {err:.3e} over {toks.size} tokens")
+    assert np.all(np.isfinite(got))
+    assert err <= TOL[c.dtype]
+    # first token of every sequence returns its own V
+    firsts = cu[:-1][np.diff(cu) > 0]
+    assert np.max(np.abs(got[firsts] - qkv[firsts, 2])) <= TOL[c.dtype]
+
+
+# ------------------------------------------------------------------ edge sweep (full oracle)
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 127, 129, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_seqlen_edges(dtype, N, causal):
+    check_dense(1, 2, 1, N, N, 64, dtype, causal, seed=N)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [8, 16, 40, 64, 72, 96, 128])
+def test_head_dims(dtype, d):
+    check_dense(2, 4, 2, 200, 200, d, dtype, True, seed=d)
+    check_dense(1, 2, 2, 77, 77, d, dtype, False, seed=d + 1)
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 32])
+def test_gqa_groups(G):
+    Hkv = 2 if G < 32 else 1
+    check_dense(1, G * Hkv, Hkv, 256, 256, 128, "bf16", True, seed=G)
+    check_dense(1, G * Hkv, Hkv, 130, 130, 64, "f16", False, seed=G + 100)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("Nq,Nk", [(1, 1000), (100, 37), (257, 1), (64, 512), (300, 129)])
+def test_cross_lengths_noncausal(dtype, Nq, Nk):
+    check_dense(1, 4, 2, Nq, Nk, 128, dtype, False, seed=Nq + Nk)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("which", ["zero", "pos", "neg", "big"])
+def test_scales(dtype, which):
+    d = 64
+    scale = {"zero": 0.0, "pos": 1 / math.sqrt(d), "neg": -1 / math.sqrt(d), "big": 2.0}[which]
+    for causal in (False, True):
+        check_dense(1, 2, 1, 150, 150, d, dtype, causal, scale=scale, seed=11)
+
+
+def test_batch_and_longer_dense():
+    check_dense(3, 8, 2, 1000, 1000, 128, "bf16", True, seed=21)
+    check_dense(2, 4, 4, 1500, 1500, 64, "f16", True, seed=22)
+    check_dense(2, 4, 1, 700, 900, 128, "bf16", False, seed=23)
+
+
+# ------------------------------------------------------------------ varlen edges
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("lengths", [
+    [5, 7], [1], [0, 3, 0], [64], [65, 1, 0, 128, 129, 2], [300, 17, 256, 1, 513],
+    [0, 0, 1000],
+])
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_edges(dtype, lengths, causal):
+    say(f"varlen {dtype} lengths={lengths} causal={causal}")
+    d = 64 if dtype != "bf16" else 128
+    qkv, cu = varlen_inputs(lengths, 3, d, seed=sum(lengths) + 1, dtype=dtype)
+    got = run_varlen(qkv, cu, dtype, causal, 1 / math.sqrt(d))
+    ref = oracle.attention_ref_varlen(qkv, cu, causal=causal, scale=1 / math.sqrt(d))
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - ref)) <= TOL[dtype]
+
+
+def test_varlen_equals_dense_per_sequence():
+    lengths = [130, 64, 1, 257]
+    d, H = 128, 4
+    qkv, cu = varlen_inputs(lengths, H, d, seed=31, dtype="bf16")
+    got = run_varlen(qkv, cu, "bf16", True, 0.1)
+    for s, L in enumerate(lengths):
+        a = int(cu[s])
+        seg = qkv[a:a + L]
+        q, k, v = (np.ascontiguousarray(seg[:, c].transpose(1, 0, 2))[None] for c in range(3))
+        dense = run_dense(q, k, v, "bf16", True, 0.1)[0].transpose(1, 0, 2)
+        assert np.max(np.abs(got[a:a + L] - dense)) <= 2 * TOL["bf16"]
+
+
+# ------------------------------------------------------------------ hygiene
+
+def test_deterministic_and_every_row_written():
+    q, k, v = dense_inputs(2, 8, 2, 517, 517, 128, seed=41, dtype="bf16")
+    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    o1 = torch.full_like(qd, float("nan"))
+    o2 = torch.full_like(qd, float("nan"))
+    aule.flash_attention(qd, kd, vd, causal=True, out=o1)
+    aule.flash_attention(qd, kd, vd, causal=True, out=o2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o1).all()
+    assert torch.equal(o1, o2)
+
+
+def test_output_guard_regions_untouched():
+    B, H, N, d = 1, 4, 333, 72
+    q, k, v = dense_inputs(B, H, H, N, N, d, seed=42, dtype="f16")
+    n = B * H * N * d
+    pad = 4096
+    buf = torch.full((n + 2 * pad,), 7.0, dtype=torch.float16, device="cuda")
+    out = buf[pad:pad + n].view(B, H, N, d)
+    aule.flash_attention(dev(q, "f16"), dev(k, "f16"), dev(v, "f16"), causal=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 7.0) and torch.all(buf[pad + n:] == 7.0)
+    ref = oracle.attention_ref(q, k, v, causal=True, scale=1 / math.sqrt(d))
+    assert np.max(np.abs(host(out) - ref)) <= TOL["f16"]
+
+
+def test_varlen_guard_regions_untouched():
+    lengths = [3, 129, 0, 64]
+    H, d = 2, 128
+    qkv, cu = varlen_inputs(lengths, H, d, seed=43, dtype="bf16")
+    T = int(cu[-1])
+    n = T * H * d
+    pad = 2048
+    buf = torch.full((n + 2 * pad,), -3.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[pad:pad + n].view(T, H, d)
+    aule.flash_attn_varlen_qkvpacked_func(dev(qkv, "bf16"), torch.from_numpy(cu).cuda(), 129,
+                                          causal=True, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == -3.0) and torch.all(buf[pad + n:] == -3.0)
+
+
+def test_non_default_stream():
+    q, k, v = dense_inputs(1, 4, 4, 256, 256, 64, seed=44, dtype="bf16")
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+        o = aule.flash_attention(qd, kd, vd, causal=True)
+    s.synchronize()
+    ref = oracle.attention_ref(q, k, v, causal=True, scale=1 / 8)
+    assert np.max(np.abs(host(o) - ref)) <= TOL["bf16"]
+
+
+def test_invalid_call_launches_nothing():
+    q, k, v = dense_inputs(1, 2, 2, 64, 64, 64, seed=45, dtype="bf16")
+    qd, kd, vd = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    o = torch.full_like(qd, 5.0)
+    st = aule.aule_attn_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), 1, 2, 2,
+                            64, 64, 64, 1, float("nan"), aule.AULE_DTYPE_BF16, 0)
+    torch.cuda.synchronize()
+    assert st == aule.AULE_ERR_INVALID_ARGUMENT
+    assert torch.all(o == 5.0)

@@ -1,0 +1,210 @@
+"""aule_attn: tiled attention forward for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over the C-ABI library ``libaule_attn.so`` (declared in
+``include/aule_attn.h``). Every step of the computation runs in the library's HIP kernels;
+this module only marshals arguments. PyTorch is used for device tensors and streams.
+
+Low-level functions carry the C names (``aule_attn_fwd``, ``aule_attn_fwd_varlen``,
+``aule_status_string``, ``aule_last_error``) and take raw device pointers. The tensor-level
+wrappers follow the pages' APIs:
+
+* ``flash_attention(q, k, v, causal=True, scale=None)`` — [batch, heads, seq, head_dim]
+  tensors, ``causal`` defaulting to True and ``scale`` to 1/sqrt(head_dim), heads_q a
+  multiple of heads_kv (jeff.news Aule-Attention article, API bullets; jdon.com
+  Aule-Attention article, GQA/MQA examples);
+* ``flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen, ...)`` — packed
+  [total_tokens, 3, heads, head_dim] with cumulative ``cu_seqlens``, ``causal`` defaulting
+  to False (ewbang.com article on a PyTorch FlashAttention for Turing, signature and
+  docstring of the varlen function; its unsupported options raise NotImplementedError).
+
+If the library is missing the import still succeeds, but every call raises: there is no
+CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libaule_attn.so")
+
+AULE_DTYPE_F32, AULE_DTYPE_F16, AULE_DTYPE_BF16 = 0, 1, 2
+AULE_OK, AULE_ERR_INVALID_ARGUMENT, AULE_ERR_UNSUPPORTED, AULE_ERR_HIP = 0, 1, 2, 3
+
+EXPORTED = ("aule_attn_fwd", "aule_attn_fwd_varlen", "aule_status_string", "aule_last_error")
+
+_lib = None
+
+
+class AuleError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{aule_status_string(status)}: {detail}")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libaule_attn.so (built by ``tiled_attention_02_amd.build``). Raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m tiled_attention_02_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    i32, vp, f32 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+    lib.aule_attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                  ctypes.c_int, vp]
+    lib.aule_attn_fwd.restype = ctypes.c_int
+    lib.aule_attn_fwd_varlen.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                         ctypes.c_int, vp]
+    lib.aule_attn_fwd_varlen.restype = ctypes.c_int
+    lib.aule_status_string.argtypes = [ctypes.c_int]
+    lib.aule_status_string.restype = ctypes.c_char_p
+    lib.aule_last_error.argtypes = []
+    lib.aule_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+# ------------------------------------------------------------------ C names
+
+def aule_attn_fwd(q, k, v, o, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
+                  causal, scale, dtype, stream=0) -> int:
+    """Raw call: device pointers as ints; returns the status code."""
+    return load_library().aule_attn_fwd(q, k, v, o, batch, heads_q, heads_kv, seqlen_q,
+                                        seqlen_k, head_dim, int(causal), float(scale),
+                                        int(dtype), stream)
+
+
+def aule_attn_fwd_varlen(qkv, cu_seqlens, o, num_seqs, total_tokens, max_seqlen, heads,
+                         head_dim, causal, scale, dtype, stream=0) -> int:
+    """Raw call: device pointers as ints; returns the status code."""
+    return load_library().aule_attn_fwd_varlen(qkv, cu_seqlens, o, num_seqs, total_tokens,
+                                               max_seqlen, heads, head_dim, int(causal),
+                                               float(scale), int(dtype), stream)
+
+
+def aule_status_string(status: int) -> str:
+    return load_library().aule_status_string(int(status)).decode()
+
+
+def aule_last_error() -> str:
+    return load_library().aule_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != AULE_OK:
+        raise AuleError(status, aule_last_error())
+
+
+# ------------------------------------------------------------------ tensor wrappers
+
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(dtype) -> int:
+    torch = _torch()
+    codes = {torch.float32: AULE_DTYPE_F32, torch.float16: AULE_DTYPE_F16,
+             torch.bfloat16: AULE_DTYPE_BF16}
+    if dtype not in codes:
+        raise TypeError(f"unsupported dtype {dtype}; use float16, bfloat16 or float32")
+    return codes[dtype]
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_gpu_tensor(name, t):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (there is no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def flash_attention(q, k, v, causal: bool = True, scale: float | None = None, out=None):
+    """O = softmax(scale * q k^T [+ causal mask]) v for q [B,Hq,N,d], k/v [B,Hkv,Nk,d]."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_gpu_tensor(name, t)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [batch, heads, seq_len, head_dim]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("k and v must be [batch, heads_kv, seq_len_k, head_dim] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_gpu_tensor("out", out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    st = aule_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv,
+                       Nq, Nk, d, causal, scale, dtype_code(q.dtype),
+                       _stream_handle(q.device))
+    _check(st)
+    return out
+
+
+def flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen, dropout_p=0.0,
+                                     softmax_scale=None, causal=False, window_size=(-1, -1),
+                                     softcap=0.0, alibi_slopes=None, deterministic=False,
+                                     return_attn_probs=False, out=None, validate=False):
+    """Varlen attention over packed qkv [total_tokens, 3, heads, head_dim] with int32
+    cu_seqlens [batch+1] on the device; returns [total_tokens, heads, head_dim].
+
+    ``validate=True`` also checks cu_seqlens against total_tokens and max_seqlen, which
+    reads it back to the host (a synchronisation)."""
+    torch = _torch()
+    if dropout_p != 0.0:
+        raise NotImplementedError("dropout is not supported")
+    if tuple(window_size) != (-1, -1):
+        raise NotImplementedError("window_size is not supported")
+    if softcap != 0.0:
+        raise NotImplementedError("softcap is not supported")
+    if alibi_slopes is not None:
+        raise NotImplementedError("alibi_slopes is not supported")
+    if return_attn_probs:
+        raise NotImplementedError("return_attn_probs is not supported")
+    _need_gpu_tensor("qkv", qkv)
+    if qkv.dim() != 4 or qkv.shape[1] != 3:
+        raise ValueError("Bad qkv shape")
+    if cu_seqlens is None or cu_seqlens.dim() != 1 or cu_seqlens.dtype != torch.int32:
+        raise ValueError("Bad cu_seqlens")
+    _need_gpu_tensor("cu_seqlens", cu_seqlens)
+    num_seqs = cu_seqlens.shape[0] - 1
+    if num_seqs <= 0:
+        raise ValueError("Bad batch size")
+    T, _, H, d = qkv.shape
+    if validate:
+        cu = cu_seqlens.cpu()
+        if int(cu[0]) != 0 or int(cu[-1]) != T:
+            raise ValueError("Token count mismatch")
+        lens = cu[1:] - cu[:-1]
+        if bool((lens < 0).any()):
+            raise ValueError("Bad cu_seqlens")
+        if T and int(lens.max()) > int(max_seqlen):
+            raise ValueError("max_seqlen is smaller than the longest sequence")
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((T, H, d), dtype=qkv.dtype, device=qkv.device)
+    st = aule_attn_fwd_varlen(qkv.data_ptr(), cu_seqlens.data_ptr(), out.data_ptr(), num_seqs,
+                              T, int(max_seqlen), H, d, causal, softmax_scale,
+                              dtype_code(qkv.dtype), _stream_handle(qkv.device))
+    _check(st)
+    return out
+
+
+__all__ = ["aule_attn_fwd", "aule_attn_fwd_varlen", "aule_status_string", "aule_last_error",
+           "flash_attention", "flash_attn_varlen_qkvpacked_func", "load_library", "AuleError",
+           "LIB_PATH", "EXPORTED"]

@@ -1,0 +1,185 @@
+// C-ABI front end: argument validation, problem description, kernel selection.
+//
+// Every check happens on the host before any HIP call, so an invalid call returns its
+// status without touching the device. Nothing here allocates or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "aule_attn.h"
+#include "attn_problem.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+aule_status_t fail(aule_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+size_t elem_size(aule_dtype_t dt) { return dt == AULE_DTYPE_F32 ? 4 : 2; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+    uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// AULE_FORCE_VALU=1 routes fp16/bf16 through the vector-ALU kernel (a debugging aid for
+// comparing the two kernels; read once per process).
+bool force_valu() {
+    static const bool v = [] {
+        const char* e = std::getenv("AULE_FORCE_VALU");
+        return e && e[0] == '1';
+    }();
+    return v;
+}
+
+aule_status_t check_common(int32_t head_dim, float scale, aule_dtype_t dtype) {
+    if (dtype != AULE_DTYPE_F32 && dtype != AULE_DTYPE_F16 && dtype != AULE_DTYPE_BF16)
+        return fail(AULE_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
+    if (head_dim <= 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "head_dim must be positive (got %d)", head_dim);
+    if (head_dim > 128 || head_dim % 8 != 0)
+        return fail(AULE_ERR_UNSUPPORTED, "head_dim must be a multiple of 8 and at most 128 (got %d)", head_dim);
+    if (!std::isfinite(scale))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "scale must be finite");
+    return AULE_OK;
+}
+
+aule_status_t dispatch(const aule::AttnProblem& p, aule_dtype_t dtype, hipStream_t stream) {
+    aule::Dtype dt = static_cast<aule::Dtype>(dtype);
+    hipError_t err;
+    if (!force_valu() && aule::mfma_supports(p, dt))
+        err = aule::launch_attn_fwd_mfma(p, dt, stream);
+    else
+        err = aule::launch_attn_fwd_valu(p, dt, stream);
+    if (err != hipSuccess)
+        return fail(AULE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    g_last_error[0] = '\0';
+    return AULE_OK;
+}
+
+const float kLog2e = 1.4426950408889634f;
+
+}  // namespace
+
+extern "C" {
+
+aule_status_t aule_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv,
+                            int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                            int32_t causal, float scale, aule_dtype_t dtype,
+                            hipStream_t stream) {
+    if (batch < 0 || seqlen_q < 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "batch and seqlen_q must be >= 0");
+    if (aule_status_t st = check_common(head_dim, scale, dtype)) return st;
+    if (heads_q <= 0 || heads_kv <= 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "heads_q and heads_kv must be positive");
+    if (heads_q % heads_kv != 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "heads_q (%d) must be a multiple of heads_kv (%d)", heads_q, heads_kv);
+    if (causal && seqlen_q != seqlen_k)
+        return fail(AULE_ERR_UNSUPPORTED, "causal attention needs seqlen_q == seqlen_k (got %d, %d)", seqlen_q, seqlen_k);
+    if (batch == 0 || seqlen_q == 0) {
+        g_last_error[0] = '\0';
+        return AULE_OK;  // empty problem
+    }
+    if (seqlen_k <= 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "seqlen_k must be positive for a non-empty problem");
+    if (!q || !k || !v || !o)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "null tensor pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)batch * heads_q * seqlen_q * head_dim * es;
+    const size_t nkv = (size_t)batch * heads_kv * seqlen_k * head_dim * es;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "output overlaps an input");
+
+    aule::AttnProblem p{};
+    p.q = q; p.k = k; p.v = v; p.o = o;
+    p.q_rstride = head_dim; p.q_hstride = (int64_t)seqlen_q * head_dim; p.q_bstride = p.q_hstride * heads_q;
+    p.k_rstride = head_dim; p.k_hstride = (int64_t)seqlen_k * head_dim; p.k_bstride = p.k_hstride * heads_kv;
+    p.v_rstride = p.k_rstride; p.v_hstride = p.k_hstride; p.v_bstride = p.k_bstride;
+    p.o_rstride = p.q_rstride; p.o_hstride = p.q_hstride; p.o_bstride = p.q_bstride;
+    p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
+    p.seqlen_q = seqlen_q; p.seqlen_k = seqlen_k; p.head_dim = head_dim;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = scale * kLog2e;
+    p.cu_seqlens = nullptr;
+    p.total_tokens = 0;
+    p.max_seqlen = seqlen_q;
+    return dispatch(p, dtype, stream);
+}
+
+aule_status_t aule_attn_fwd_varlen(const void* qkv, const int32_t* cu_seqlens, void* o,
+                                   int32_t num_seqs, int32_t total_tokens,
+                                   int32_t max_seqlen, int32_t heads, int32_t head_dim,
+                                   int32_t causal, float scale, aule_dtype_t dtype,
+                                   hipStream_t stream) {
+    if (total_tokens < 0 || max_seqlen < 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "total_tokens and max_seqlen must be >= 0");
+    if (num_seqs <= 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "num_seqs must be positive (got %d)", num_seqs);
+    if (heads <= 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "heads must be positive");
+    if (aule_status_t st = check_common(head_dim, scale, dtype)) return st;
+    if (total_tokens == 0) {
+        g_last_error[0] = '\0';
+        return AULE_OK;  // every sequence is empty
+    }
+    if (!qkv || !cu_seqlens || !o)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(qkv) || !aligned16(o) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "qkv/o must be 16-byte aligned, cu_seqlens 4-byte aligned");
+    const size_t es = elem_size(dtype);
+    const size_t nqkv = (size_t)total_tokens * 3 * heads * head_dim * es;
+    const size_t no = (size_t)total_tokens * heads * head_dim * es;
+    if (overlaps(o, no, qkv, nqkv) || overlaps(o, no, cu_seqlens, (size_t)(num_seqs + 1) * 4))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "output overlaps an input");
+    if ((int64_t)total_tokens + num_seqs > INT32_MAX)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "too many tokens");
+
+    const int64_t hd = (int64_t)heads * head_dim;
+    const char* base = static_cast<const char*>(qkv);
+    aule::AttnProblem p{};
+    p.q = base;
+    p.k = base + hd * es;
+    p.v = base + 2 * hd * es;
+    p.o = o;
+    p.q_rstride = p.k_rstride = p.v_rstride = 3 * hd;
+    p.q_hstride = p.k_hstride = p.v_hstride = head_dim;
+    p.q_bstride = p.k_bstride = p.v_bstride = 0;
+    p.o_rstride = hd; p.o_hstride = head_dim; p.o_bstride = 0;
+    p.batch = num_seqs; p.heads_q = heads; p.heads_kv = heads; p.group = 1;
+    p.seqlen_q = max_seqlen; p.seqlen_k = max_seqlen; p.head_dim = head_dim;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = scale * kLog2e;
+    p.cu_seqlens = cu_seqlens;
+    p.total_tokens = total_tokens;
+    p.max_seqlen = max_seqlen;
+    return dispatch(p, dtype, stream);
+}
+
+const char* aule_status_string(aule_status_t status) {
+    switch (status) {
+        case AULE_OK: return "AULE_OK";
+        case AULE_ERR_INVALID_ARGUMENT: return "AULE_ERR_INVALID_ARGUMENT";
+        case AULE_ERR_UNSUPPORTED: return "AULE_ERR_UNSUPPORTED";
+        case AULE_ERR_HIP: return "AULE_ERR_HIP";
+    }
+    return "AULE_STATUS_UNKNOWN";
+}
+
+const char* aule_last_error(void) { return g_last_error; }
+
+}  // extern "C"
