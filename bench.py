@@ -37,6 +37,9 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and report them on stderr")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
 
 
@@ -142,6 +145,16 @@ def main():
         sys.exit(2)
     import torch
     from workloads import CONFIGS
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20)
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": max(1, args.steps)}), flush=True)
+        return
 
     cfg = CONFIGS[args.workload]
     dev_in, host_in = device_inputs(cfg, torch)

@@ -27,7 +27,8 @@ import math
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libaule_attn.so")
+# AULE_LIB points the binding at another build of the same library (variant comparisons)
+LIB_PATH = os.environ.get("AULE_LIB") or os.path.join(_PKG, "libaule_attn.so")
 
 AULE_DTYPE_F32, AULE_DTYPE_F16, AULE_DTYPE_BF16 = 0, 1, 2
 AULE_OK, AULE_ERR_INVALID_ARGUMENT, AULE_ERR_UNSUPPORTED, AULE_ERR_HIP = 0, 1, 2, 3

@@ -49,9 +49,11 @@ def _compile(src: str, obj: str, extra: list[str]) -> None:
         sys.stderr.write("\n".join(msgs) + "\n")
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
+def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str | None = None) -> str:
+    """Compile every source and link the library (to `out`, default the in-tree path)."""
     extra = list(extra_flags or [])
-    objdir = os.path.join(PKG, "_build")
+    lib = out or LIB
+    objdir = os.path.join(PKG, "_build" if out is None else "_build_" + os.path.basename(lib).replace(".", "_"))
     os.makedirs(objdir, exist_ok=True)
     jobs = []
     for s in SOURCES:
@@ -60,16 +62,21 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         jobs.append((src, obj))
     with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
         list(ex.map(lambda j: _compile(j[0], j[1], extra), jobs))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + [o for _, o in jobs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import argparse
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--out", default=None, help="library path (default: in-tree libaule_attn.so)")
+    ap.add_argument("-D", "--define", action="append", default=[], help="extra preprocessor define")
+    a = ap.parse_args()
+    build(verbose=True, extra_flags=["-D" + d for d in a.define], out=a.out)

@@ -41,6 +41,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <cstdlib>
+
 #include "attn_device.h"
 
 namespace aule {
@@ -54,11 +56,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
-constexpr int kBN = 64;               // keys per K/V tile
-constexpr int kRowsPerWave = 64;      // two 32-row blocks
+constexpr int kBN = 64;               // keys per K/V tile (two 32-key sub-steps)
 [[maybe_unused]] constexpr float kRescaleSlack = 8.0f; // log2 units
 
 template <typename T> struct Mfma;
@@ -67,9 +67,9 @@ template <> struct Mfma<bf16_t> {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
     }
+    // two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
     static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-        bf16_t a = static_cast<bf16_t>(lo), b = static_cast<bf16_t>(hi);
-        return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
     }
     // acc + lo + hi of a packed pair, in fp32 (v_dot2 against (1, 1))
     static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
@@ -82,9 +82,9 @@ template <> struct Mfma<f16_t> {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     }
+    // two fp32 -> packed fp16 pair, round to nearest even (one v_cvt_pk_f16_f32)
     static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-        f16_t a = static_cast<f16_t>(lo), b = static_cast<f16_t>(hi);
-        return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
     }
     static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
         const f16x2 one = {(f16_t)1.0f, (f16_t)1.0f};
@@ -133,22 +133,26 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_b
 }
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <typename T, int D, int GH, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// WAVES waves per workgroup (4: one per SIMD, 8: two per SIMD so one wave's softmax runs
+// while the other's matrix products do); each wave owns NB blocks of 32 query rows of one
+// query head.
+template <typename T, int D, int WAVES, int NB, int GH, bool PIPE, bool CAUSAL, bool VARLEN>
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WAVES / 4)))
 void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
-    constexpr int RB = kWaves / GH;              // 64-row blocks per workgroup
+    constexpr int kThreads = WAVES * 64;
+    constexpr int kRowsPerWave = 32 * NB;
+    constexpr int RB = WAVES / GH;               // row blocks per workgroup
     constexpr int BMW = kRowsPerWave * RB;       // query rows per workgroup
     constexpr int KC = D / 8;                    // 16-byte chunks per K / V row
     constexpr int KS = D / 16;                   // k-steps of S^T = K Q^T
     constexpr int DB = D / 32;                   // 32-row d-blocks of O^T
-    constexpr int NB = 2;                        // 32-query blocks per wave
     constexpr int TILE_CHUNKS = kBN * KC;        // 16-byte chunks per K (or V) tile
     constexpr int NI = TILE_CHUNKS / kThreads;   // load instructions per wave per tile
     static_assert(NI >= 1 && TILE_CHUNKS % kThreads == 0, "tile must split evenly over the waves");
 
-    __shared__ u32x4 sK0[TILE_CHUNKS], sK1[TILE_CHUNKS];
-    __shared__ u32x4 sV0[TILE_CHUNKS], sV1[TILE_CHUNKS];
+    __shared__ u32x4 sK0[TILE_CHUNKS], sK1[TILE_CHUNKS], sK2[TILE_CHUNKS];
+    __shared__ u32x4 sV0[TILE_CHUNKS], sV1[TILE_CHUNKS], sV2[TILE_CHUNKS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -165,14 +169,24 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         bidx = s.seq; tok0 = s.tok0; tile = s.tile; Lq = s.len_q; Lk = s.len_k;
         hq0 = blockIdx.y * GH;
     } else {
+        // groups = (batch, GH query heads sharing one kv head). Workgroup x runs on XCD
+        // x % 8; when the groups split evenly, each XCD gets whole groups so their K/V stay
+        // in that XCD's L2. Within an XCD (or the whole grid) the longest causal tiles go first.
         const int ngroups = p.heads_q / GH;
-        const int per_tile = p.batch * ngroups;
+        const int NG = p.batch * ngroups;
         const int x = blockIdx.x;
-        const int t = x / per_tile;
-        const int rest = x - t * per_tile;
-        tile = CAUSAL ? (n_qtiles - 1 - t) : t;     // longest causal tiles first
-        bidx = rest / ngroups;
-        hq0 = (rest - bidx * ngroups) * GH;
+        int t, g;
+        if (NG % 8 == 0) {
+            const int per = NG / 8, xcd = x & 7, l = x >> 3;
+            t = l / per;
+            g = xcd * per + (l - t * per);
+        } else {
+            t = x / NG;
+            g = x - t * NG;
+        }
+        tile = CAUSAL ? (n_qtiles - 1 - t) : t;
+        bidx = g / ngroups;
+        hq0 = (g - bidx * ngroups) * GH;
         Lq = p.seqlen_q; Lk = p.seqlen_k;
     }
     const int hq = hq0 + (wave % GH);
@@ -221,12 +235,14 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         }
     }
 
-    // ---------------------------------------------------------------- tile ranges
+    // ---------------------------------------------------------------- sub-step ranges
+    // The key range is walked in 32-key sub-steps; sub-steps 2t and 2t+1 live in K/V tile t.
+    // All waves of the workgroup walk the same sub-steps (a wave whose own rows end earlier
+    // gets fully masked sub-steps at the end, which add exact zeros).
     const int wg_rows_end = min(tile * BMW + BMW, Lq);
-    const int n_kt = CAUSAL ? (wg_rows_end - 1) / kBN + 1 : (Lk + kBN - 1) / kBN;
-    int wave_last;   // last K/V tile this wave computes on (-1: none)
-    if (qr0 >= Lq) wave_last = -1;
-    else wave_last = CAUSAL ? (min(qr0 + kRowsPerWave, Lq) - 1) / kBN : n_kt - 1;
+    const int keys_needed = CAUSAL ? wg_rows_end : Lk;
+    const int nsub = (keys_needed + 31) / 32;
+    const int n_kt = (nsub + 1) / 2;
 
     // ---------------------------------------------------------------- accumulators
     f32x16 o[DB][NB];
@@ -238,123 +254,260 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) { m_ref[nb] = -INFINITY; l_part[nb] = 0.f; }
 
-    // lane constants of the transposed V reads
-    const int tg = lane >> 4, tc = lane & 15;
-    const int t_key = 8 * (tg >> 1) + (tc >> 2);          // + 16*kc + 4*t
-    const int t_chunk = 2 * (tg & 1) + ((tc & 3) >> 1);   // + 4*db
-    const int t_within = (tc & 1) * 8;                     // bytes
+    // Per-lane LDS address terms of the fragment reads. They are rebuilt from `lane` where
+    // they are used; pinning `lane` with an empty asm per iteration stops the compiler from
+    // hoisting every buffer's addresses into registers for the whole loop.
+    struct LaneAddr { int krow_sig, kx, h, tv_key, tv_chunk, tv_within, tv_swz; };
+    auto lane_addr = [&](int ln_raw) {
+        LaneAddr a;
+        const int l32 = ln_raw & 31, tg = ln_raw >> 4, tc = ln_raw & 15;
+        a.krow_sig = sigma(l32);
+        a.kx = l32 & (KC - 1);
+        a.h = ln_raw >> 5;
+        a.tv_key = 8 * (tg >> 1) + (tc >> 2);          // + 16*kc + 4*t
+        a.tv_chunk = 2 * (tg & 1) + ((tc & 3) >> 1);   // + 4*db
+        a.tv_within = (tc & 1) * 8;                    // bytes
+        a.tv_swz = vswz<KC>(a.tv_key);                 // (16*kc + 4*t + tv_key) % 4 == tv_key % 4
+        return a;
+    };
 
-    auto compute_tile = [&](int j, const u32x4* cK, const u32x4* cV) {
-        // two 32-key sub-steps per LDS tile keep the live S / P registers small; the
-        // online softmax is exact at any step size
+    // S^T = K Q^T for sub-step `sub` (32 keys x 32*NB queries) from K tile buffer cK
+    auto qk = [&](int sub, const u32x4* cK, f32x16 (&acc)[NB], const LaneAddr& la) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int k0 = j * kBN + 32 * mb;
-            if (CAUSAL && k0 > qr0 + kRowsPerWave - 1) continue;   // all keys in the future
-            // S^T = K Q^T: 32 keys x 64 queries
-            f32x16 s[NB];
+        for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
+        const int krow = 32 * (sub & 1) + la.krow_sig;
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) s[nb] = f32x16{};
-            const int krow = 32 * mb + sigma(ln);
+        for (int ks = 0; ks < KS; ++ks) {
+            const u32x4 a = cK[krow * KC + ((2 * ks + la.h) ^ la.kx)];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x4 a = cK[krow * KC + ((2 * ks + h) ^ (ln & (KC - 1)))];
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) s[nb] = Mfma<T>::mma(a, qf[nb][ks], s[nb]);
-            }
-            // mask keys past the end and (causal) keys after the query
-            const bool need_mask = (k0 + 32 > Lk) || (CAUSAL && k0 + 31 > qr0);
-            if (need_mask) {
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) {
-                    const int qi = qr0 + 32 * nb + ln;
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + 16 * (r >> 3) + 8 * h + (r & 7);
-                        const bool masked = (key >= Lk) || (CAUSAL && key > qi);
-                        if (masked) s[nb][r] = -INFINITY;
-                    }
-                }
-            }
-            // online softmax per 32-query block
-            u32x4 pf[2][NB];   // [16-key chunk][nb] packed P^T operands
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = Mfma<T>::mma(a, qf[nb][ks], acc[nb]);
+        }
+    };
+    // -inf for keys past the end and (causal) keys after the query; a uniform branch
+    auto mask = [&](int sub, f32x16 (&acc)[NB]) {
+        const int k0 = 32 * sub;
+        if ((k0 + 32 > Lk) || (CAUSAL && k0 + 31 > qr0)) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                float mx = -INFINITY;
+                const int qi = qr0 + 32 * nb + ln;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-                const bool raise = mt > m_ref[nb] + kRescaleSlack;
-                if (__any(raise)) {
-                    const float m_new = fmaxf(m_ref[nb], mt);
-                    const float alpha = __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
-                    l_part[nb] *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) o[db][nb] *= alpha;
-                    m_ref[nb] = m_new;
-                }
-                const float mneg = -m_ref[nb];
-                float lsum = 0.f;
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    float pv[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) pv[e] = __builtin_amdgcn_exp2f(fmaf(s[nb][8 * cc + e], c, mneg));
-                    const u32x4 pk = {Mfma<T>::pack2(pv[0], pv[1]), Mfma<T>::pack2(pv[2], pv[3]),
-                                      Mfma<T>::pack2(pv[4], pv[5]), Mfma<T>::pack2(pv[6], pv[7])};
-                    // the row sum uses the same rounded P that multiplies V, so O stays an
-                    // exact convex combination of V rows up to fp32 accumulation
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) lsum = Mfma<T>::sum2(pk[w], lsum);
-                    pf[cc][nb] = pk;
-                }
-                l_part[nb] += lsum;
-            }
-            // O^T += V^T P^T over these 32 keys
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const int kc = 2 * mb + cc;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    u32x4 a;
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int key = 16 * kc + 4 * t + t_key;
-                        const int chunk = (4 * db + t_chunk) ^ vswz<KC>(key);
-                        const char* addr = reinterpret_cast<const char*>(cV + key * KC + chunk) + t_within;
-                        const i16x4_t part = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4*)(const_cast<char*>(addr)));
-                        const u32x2 w = __builtin_bit_cast(u32x2, part);
-                        a[2 * t] = w[0];
-                        a[2 * t + 1] = w[1];
-                    }
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) o[db][nb] = Mfma<T>::mma(a, pf[cc][nb], o[db][nb]);
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 16 * (r >> 3) + 8 * h + (r & 7);
+                    const bool masked = (key >= Lk) || (CAUSAL && key > qi);
+                    acc[nb][r] = masked ? -INFINITY : acc[nb][r];
                 }
             }
         }
     };
+    // O^T += V^T P^T for sub-step `sub` from V tile buffer cV
+    auto pv = [&](int sub, const u32x4* cV, const u32x4 (&pf)[2][NB], const LaneAddr& la) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const int kc = 2 * (sub & 1) + cc;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                u32x4 a;
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int key = 16 * kc + 4 * t + la.tv_key;
+                    const char* addr = reinterpret_cast<const char*>(cV + key * KC + ((4 * db + la.tv_chunk) ^ la.tv_swz)) + la.tv_within;
+                    const i16x4_t part = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<char*>(addr)));
+                    const u32x2 w = __builtin_bit_cast(u32x2, part);
+                    a[2 * t] = w[0];
+                    a[2 * t + 1] = w[1];
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) o[db][nb] = Mfma<T>::mma(a, pf[cc][nb], o[db][nb]);
+            }
+        }
+    };
+    // online softmax of one sub-step: P (packed 16-bit) relative to the possibly raised
+    // reference max; the O / l rescale is applied by finish() after this sub-step's
+    // neighbours in the pipeline have been issued
+    struct Soft { float m_new[NB], alpha[NB], lsum[NB]; bool raise[NB]; };
+    auto softmax = [&](const f32x16 (&acc)[NB], u32x4 (&pf)[2][NB], Soft& st) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[nb][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+            const bool any = __any(mt > m_ref[nb] + kRescaleSlack);
+            const float m_new = any ? fmaxf(m_ref[nb], mt) : m_ref[nb];
+            st.raise[nb] = any;
+            st.m_new[nb] = m_new;
+            st.alpha[nb] = __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
+            const float mneg = -m_new;
+            float lsum = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                float pv8[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv8[e] = __builtin_amdgcn_exp2f(fmaf(acc[nb][8 * cc + e], c, mneg));
+                const u32x4 pk = {Mfma<T>::pack2(pv8[0], pv8[1]), Mfma<T>::pack2(pv8[2], pv8[3]),
+                                  Mfma<T>::pack2(pv8[4], pv8[5]), Mfma<T>::pack2(pv8[6], pv8[7])};
+                // the row sum uses the same rounded P that multiplies V, so O stays an
+                // exact convex combination of V rows up to fp32 accumulation
+#pragma unroll
+                for (int w = 0; w < 4; ++w) lsum = Mfma<T>::sum2(pk[w], lsum);
+                pf[cc][nb] = pk;
+            }
+            st.lsum[nb] = lsum;
+        }
+    };
+    auto finish = [&](const Soft& st) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            if (st.raise[nb]) {
+                l_part[nb] *= st.alpha[nb];
+#pragma unroll
+                for (int db = 0; db < DB; ++db) o[db][nb] *= st.alpha[nb];
+            }
+            l_part[nb] += st.lsum[nb];
+            m_ref[nb] = st.m_new[nb];
+        }
+    };
 
-    // ---------------------------------------------------------------- main loop
-    // Even tiles live in buffers 0, odd tiles in buffers 1; the copy of tile j+1 is in
-    // flight while tile j is computed.
+    // ---------------------------------------------------------------- pipelined main loop
+    // Iteration i issues, in one basic block, the matrix products of S(i+1) = K Q^T and of
+    // O += V^T P(i-1) together with the softmax of S(i), so the vector ALU work of one
+    // sub-step overlaps the matrix-core work of its neighbours. K/V tiles are triple
+    // buffered (tile t in buffer t % 3): the copy of tile t+1 starts at the barrier before
+    // the first iteration that reads tile t and must land by the next such barrier, one
+    // tile later; by then tile t-2, which shared its buffer, has been read for the last
+    // time. Iterations are unrolled by six so every buffer choice is a compile-time one.
     const uint32_t tk = kBN * k_rs, tv = kBN * v_rs;   // bytes per K / V tile
-    lds_void* const lK0 = (lds_void*)sK0;
-    lds_void* const lK1 = (lds_void*)sK1;
-    lds_void* const lV0 = (lds_void*)sV0;
-    lds_void* const lV1 = (lds_void*)sV1;
-    issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, 0, 0, lK0, lV0, wave);
+    lds_void* const lK[3] = {(lds_void*)sK0, (lds_void*)sK1, (lds_void*)sK2};
+    lds_void* const lV[3] = {(lds_void*)sV0, (lds_void*)sV1, (lds_void*)sV2};
+    const u32x4* const cKb[3] = {sK0, sK1, sK2};
+    const u32x4* const cVb[3] = {sV0, sV1, sV2};
+
+    f32x16 s_cur[NB], s_nxt[NB];
+    u32x4 p_prev[2][NB], p_cur[2][NB];
+
+    if constexpr (!PIPE) {
+        // Straight loop: per 32-key sub-step S = K Q^T, mask, softmax, P V. Tile t sits in
+        // buffer t % 3; the copy of tile t+1 starts at the barrier before tile t is read
+        // (its buffer last held tile t-2, finished before the previous barrier).
+        issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, 0, 0, lK[0], lV[0], wave);
+        for (int g = 0; 3 * g < n_kt; ++g) {
+#pragma unroll
+            for (int u = 0; u < 3; ++u) {
+                const int t = 3 * g + u;
+                if (t >= n_kt) break;
+                __syncthreads();
+                if (t + 1 < n_kt)
+                    issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, (t + 1) * tk, (t + 1) * tv,
+                                   lK[(u + 1) % 3], lV[(u + 1) % 3], wave);
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int i = 2 * t + half;
+                    if (i >= nsub) break;
+                    const LaneAddr la = lane_addr(lane);
+                    qk(i, cKb[u], s_cur, la);
+                    mask(i, s_cur);
+                    Soft st;
+                    softmax(s_cur, p_cur, st);
+                    finish(st);
+                    pv(i, cVb[u], p_cur, la);
+                }
+            }
+        }
+    } else {
+
+    // Instruction order of a full iteration (one basic block): a few LDS fragment reads up
+    // front, then groups of one MFMA, a slice of the softmax VALU work and the next LDS
+    // reads, so the matrix core and the vector ALU stay busy together and the fragment
+    // registers stay short-lived.
+    auto interleave = [&]() {
+        constexpr int kMfma = NB * (KS + 2 * DB);      // matrix products per iteration
+        constexpr int kDs = KS + 4 * DB;               // LDS fragment reads per iteration
+        constexpr int kValu = (48 * NB + 32 + kMfma - 1) / kMfma;
+        constexpr int kDsPer = (kDs - 4 + kMfma - 1) / kMfma;
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int k = 0; k < kMfma; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, kDsPer, 0);
+        }
+    };
+
+    issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, 0, 0, lK[0], lV[0], wave);
     __syncthreads();
-    for (int j = 0; j < n_kt; j += 2) {
-        if (j + 1 < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, (j + 1) * tk, (j + 1) * tv, lK1, lV1, wave);
-        if (j <= wave_last) compute_tile(j, sK0, sV0);
-        __syncthreads();
-        if (j + 1 >= n_kt) break;
-        if (j + 2 < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, (j + 2) * tk, (j + 2) * tv, lK0, lV0, wave);
-        if (j + 1 <= wave_last) compute_tile(j + 1, sK1, sV1);
-        __syncthreads();
+    if (n_kt > 1) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, tk, tv, lK[1], lV[1], wave);
+    qk(0, cKb[0], s_cur, lane_addr(lane));
+    mask(0, s_cur);
+    {
+        Soft st;
+        if (nsub > 1) {
+            qk(1, cKb[0], s_nxt, lane_addr(lane));
+            softmax(s_cur, p_cur, st);
+        } else {
+            softmax(s_cur, p_cur, st);
+        }
+        finish(st);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) p_prev[cc][nb] = p_cur[cc][nb];
+        if (nsub > 1) {
+            mask(1, s_nxt);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) s_cur[nb] = s_nxt[nb];
+        }
     }
+    for (int g = 0; 6 * g + 1 < nsub; ++g) {
+#pragma unroll
+        for (int u = 1; u <= 6; ++u) {
+            const int i = 6 * g + u;
+            if (i >= nsub) break;
+            const int kb = ((u + 1) / 2) % 3;     // buffer of tile (i+1)/2
+            const int vbuf = ((u - 1) / 2) % 3;   // buffer of tile (i-1)/2
+            if (u & 1) {
+                const int t = (i + 1) / 2;         // first iteration that reads tile t
+                if (t < n_kt) {
+                    __syncthreads();               // tile t landed; tile t-2 fully read
+                    if (t + 1 < n_kt)
+                        issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, (t + 1) * tk, (t + 1) * tv,
+                                       lK[(kb + 1) % 3], lV[(kb + 1) % 3], wave);
+                }
+            }
+            int lane_o = lane;
+            asm volatile("" : "+v"(lane_o));
+            const LaneAddr la = lane_addr(lane_o);
+            Soft st;
+            if (i + 1 < nsub) {
+                qk(i + 1, cKb[kb], s_nxt, la);
+                pv(i - 1, cVb[vbuf], p_prev, la);
+                softmax(s_cur, p_cur, st);
+#ifndef AULE_NO_INTERLEAVE
+                interleave();
+#endif
+            } else {
+                pv(i - 1, cVb[vbuf], p_prev, la);
+                softmax(s_cur, p_cur, st);
+            }
+            finish(st);
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) p_prev[cc][nb] = p_cur[cc][nb];
+            if (i + 1 < nsub) {
+                mask(i + 1, s_nxt);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) s_cur[nb] = s_nxt[nb];
+            }
+        }
+    }
+    // the last sub-step's P^T V
+    {
+        const int last = nsub - 1;
+        const int lb = (last / 2) % 3;
+        pv(last, lb == 0 ? cVb[0] : lb == 1 ? cVb[1] : cVb[2], p_prev, lane_addr(lane));
+    }
+    }  // PIPE
 
     // ---------------------------------------------------------------- epilogue
 #pragma unroll
@@ -382,30 +535,46 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 
 int heads_per_group(int group) { return (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1; }
 
-template <typename T, int D, int GH, bool CAUSAL, bool VARLEN>
+int mfma_shape() {
+    static const int v = [] {
+        const char* e = std::getenv("AULE_MFMA_SHAPE");
+        const int v = e ? std::atoi(e) : 0;
+        return (v >= 0 && v <= 1) ? v : 0;
+    }();
+    return v;
+}
+
+template <typename T, int D, int WAVES, int NB, int GH, bool PIPE, bool CAUSAL, bool VARLEN>
 hipError_t launch_cfg(const AttnProblem& p, hipStream_t stream) {
-    constexpr int BMW = kRowsPerWave * (kWaves / GH);
-    dim3 block(kThreads);
+    constexpr int BMW = 32 * NB * (WAVES / GH);
+    dim3 block(WAVES * 64);
     if constexpr (VARLEN) {
         dim3 grid(varlen_grid_tiles(p.total_tokens, p.batch, BMW), p.heads_q / GH, 1);
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, GH, CAUSAL, true>), grid, block, 0, stream, p, 0);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, PIPE, CAUSAL, true>), grid, block, 0, stream, p, 0);
     } else {
         const int n_qtiles = (p.seqlen_q + BMW - 1) / BMW;
         const int64_t nblocks = (int64_t)n_qtiles * p.batch * (p.heads_q / GH);
         if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
         dim3 grid((unsigned)nblocks);
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, GH, CAUSAL, false>), grid, block, 0, stream, p, n_qtiles);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, PIPE, CAUSAL, false>), grid, block, 0, stream, p, n_qtiles);
     }
     return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_gh(const AttnProblem& p, hipStream_t stream) {
-    switch (VARLEN ? 1 : heads_per_group(p.group)) {
-        case 4: return launch_cfg<T, D, 4, CAUSAL, VARLEN>(p, stream);
-        case 2: return launch_cfg<T, D, 2, CAUSAL, VARLEN>(p, stream);
-        default: return launch_cfg<T, D, 1, CAUSAL, VARLEN>(p, stream);
+    // kernel shape: 8 waves x 32 rows; AULE_MFMA_SHAPE=1 selects the software-pipelined
+    // loop instead of the straight one
+    const int gh = VARLEN ? 1 : heads_per_group(p.group);
+    switch ((mfma_shape() == 1 ? 3 : 0) + (gh == 4 ? 2 : gh == 2 ? 1 : 0)) {
+        case 0: return launch_cfg<T, D, 8, 1, 1, false, CAUSAL, VARLEN>(p, stream);
+        case 1: return launch_cfg<T, D, 8, 1, 2, false, CAUSAL, VARLEN>(p, stream);
+        case 2: return launch_cfg<T, D, 8, 1, 4, false, CAUSAL, VARLEN>(p, stream);
+        case 3: return launch_cfg<T, D, 8, 1, 1, true, CAUSAL, VARLEN>(p, stream);
+        case 4: return launch_cfg<T, D, 8, 1, 2, true, CAUSAL, VARLEN>(p, stream);
+        case 5: return launch_cfg<T, D, 8, 1, 4, true, CAUSAL, VARLEN>(p, stream);
     }
+    return hipErrorInvalidValue;
 }
 
 template <typename T, int D>
@@ -429,7 +598,7 @@ bool mfma_supports(const AttnProblem& p, Dtype dt) {
     // slice plus one tile of offset headroom below 2^30 bytes.
     const int64_t rows = p.cu_seqlens ? p.total_tokens : p.seqlen_k;
     const int64_t stride = p.k_rstride > p.v_rstride ? p.k_rstride : p.v_rstride;
-    const int64_t bytes = (rows + kBN) * stride * 2;
+    const int64_t bytes = (rows + 128) * stride * 2;
     return bytes < (int64_t(1) << 30);
 }
 
