@@ -24,6 +24,35 @@ sys.path.insert(0, ROOT)
 
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense, published
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["tiled_attention_02_amd/csrc/attn_fwd_mfma.hip",
+                  "tiled_attention_02_amd/csrc/attn_device.h",
+                  "tiled_attention_02_amd/csrc/attn_problem.h",
+                  "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE record, scaled
+    by the copy-kernel calibration; None when the record is absent, for another workload, or
+    taken on kernel sources that have changed since."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("workload") != workload or rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    kib = rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]
+    return int(kib * 1024)
 
 
 def parse():
@@ -37,6 +66,8 @@ def parse():
                     help="approximate CPU time budget of the oracle sample")
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and report them on stderr")
+    ap.add_argument("--print-kernel-hash", action="store_true",
+                    help="print the hash of the kernel sources the traffic record is keyed to")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -139,6 +170,9 @@ def cpu_baseline(cfg, host_inputs, budget_s):
 
 def main():
     args = parse()
+    if args.print_kernel_hash:
+        print(kernel_source_hash())
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -180,7 +214,8 @@ def main():
         "data": "synthetic (seeded N(0,1) inputs)",
         "config": {"workload": cfg.name, "desc": describe(cfg), "pct_of_peak": round(100 * value / peak, 2)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(cfg.name),
                      "kernel_ms": round(kern_s * 1e3, 4),
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": cfg.bytes_compulsory()},

@@ -136,7 +136,7 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_b
 // WAVES waves per workgroup (4: one per SIMD, 8: two per SIMD so one wave's softmax runs
 // while the other's matrix products do); each wave owns NB blocks of 32 query rows of one
 // query head.
-template <typename T, int D, int WAVES, int NB, int GH, bool PIPE, bool CAUSAL, bool VARLEN>
+template <typename T, int D, int WAVES, int NB, int GH, int LOOP, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WAVES / 4)))
 void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -276,12 +276,27 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
         const int krow = 32 * (sub & 1) + la.krow_sig;
+#if defined(AULE_QK_PREFETCH)
+        u32x4 af[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) af[ks] = cK[krow * KC + ((2 * ks + la.h) ^ la.kx)];
+#endif
+#if defined(AULE_SETPRIO)
+        __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
+#if defined(AULE_QK_PREFETCH)
+            const u32x4 a = af[ks];
+#else
             const u32x4 a = cK[krow * KC + ((2 * ks + la.h) ^ la.kx)];
+#endif
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[nb] = Mfma<T>::mma(a, qf[nb][ks], acc[nb]);
         }
+#if defined(AULE_SETPRIO)
+        __builtin_amdgcn_s_setprio(0);
+#endif
     };
     // -inf for keys past the end and (causal) keys after the query; a uniform branch
     auto mask = [&](int sub, f32x16 (&acc)[NB]) {
@@ -301,6 +316,9 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     };
     // O^T += V^T P^T for sub-step `sub` from V tile buffer cV
     auto pv = [&](int sub, const u32x4* cV, const u32x4 (&pf)[2][NB], const LaneAddr& la) {
+#if defined(AULE_SETPRIO)
+        __builtin_amdgcn_s_setprio(1);
+#endif
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             const int kc = 2 * (sub & 1) + cc;
@@ -320,6 +338,9 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                 for (int nb = 0; nb < NB; ++nb) o[db][nb] = Mfma<T>::mma(a, pf[cc][nb], o[db][nb]);
             }
         }
+#if defined(AULE_SETPRIO)
+        __builtin_amdgcn_s_setprio(0);
+#endif
     };
     // online softmax of one sub-step: P (packed 16-bit) relative to the possibly raised
     // reference max; the O / l rescale is applied by finish() after this sub-step's
@@ -386,20 +407,88 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     f32x16 s_cur[NB], s_nxt[NB];
     u32x4 p_prev[2][NB], p_cur[2][NB];
 
-    if constexpr (!PIPE) {
-        // Straight loop: per 32-key sub-step S = K Q^T, mask, softmax, P V. Tile t sits in
-        // buffer t % 3; the copy of tile t+1 starts at the barrier before tile t is read
-        // (its buffer last held tile t-2, finished before the previous barrier).
+    if constexpr (LOOP == 2) {
+        // Ping-pong: the two waves of a SIMD (groups 0 and 1) alternate between a matrix
+        // block M_m = {O += V^T P(m-1), S(m) = K Q^T} and a softmax block V_v, with a
+        // workgroup barrier between phases. In phase p the group (p & 1) runs M_{p/2}
+        // while the other group runs V_{p/2 - 1 + (p & 1)}, so one wave's vector work
+        // hides under the other's matrix work. Tile t is read from phase 4t to phase 4t+5;
+        // with three buffers the copy of tile t+2 starts at phase 4t+2 (tile t-1, its
+        // buffer's previous tile, was last read in phase 4t+1) and is waited for at the
+        // barrier before phase 4(t+2), when only the copy of tile t+3 may be newer.
+        const int grp = (wave >> p.pp_shift) & 1;
+        f32x16 sb[NB];
+        u32x4 pb[2][NB];
+        auto phase_barrier = [&](bool wait_tile, bool newer_pending) {
+            if (wait_tile) {
+                if (newer_pending) {
+                    if constexpr (NI == 2) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                    else asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                }
+            } else {
+                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            }
+        };
         issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, 0, 0, lK[0], lV[0], wave);
+        if (n_kt > 1) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, tk, tv, lK[1], lV[1], wave);
+        phase_barrier(true, n_kt > 1);
+        const int nphase = 2 * nsub + 2;
+        for (int pg = 0; pg < nphase; pg += 12) {
+#pragma unroll
+            for (int q = 0; q < 12; ++q) {
+                const int ph = pg + q;
+                if (ph >= nphase) break;
+                const int m = ph >> 1;
+                if ((q & 3) == 2) {                           // phase 4u+2: copy tile u+2
+                    const int t2 = (ph >> 2) + 2;
+                    const int b2 = ((q >> 2) + 2) % 3;
+                    if (t2 < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, t2 * tk, t2 * tv, lK[b2], lV[b2], wave);
+                }
+                if (grp == (q & 1)) {
+                    // M_m: P(m-1) V and S(m) = K Q^T
+                    const int kbuf = (q >> 2) % 3;            // tile m/2  (m/2 == ph/4)
+                    const int vbuf = ((q + 10) >> 2) % 3;     // tile (m-1)/2 == (ph-2)/4, mod 3
+                    const LaneAddr la = lane_addr(lane);
+                    if (m < nsub) qk(m, cKb[kbuf], sb, la);
+                    if (m >= 1 && m - 1 < nsub) pv(m - 1, cVb[vbuf], pb, la);
+                } else {
+                    const int v = m - 1 + (q & 1);
+                    if (v >= 0 && v < nsub) {
+                        mask(v, sb);
+                        Soft st;
+                        softmax(sb, pb, st);
+                        finish(st);
+                    }
+                }
+                const bool period_end = (q & 3) == 3;         // next phase starts tile (ph+1)/4
+                const int tn = (ph + 1) >> 2;
+                phase_barrier(period_end && tn < n_kt, tn + 1 < n_kt);
+            }
+        }
+    } else if constexpr (LOOP == 0) {
+        // Straight loop: per 32-key sub-step S = K Q^T, mask, softmax, P V. Tile t sits in
+        // buffer t % 3. At the barrier before tile t each wave waits only for its copy of
+        // tile t (the copy of tile t+1 may still be in flight), then starts the copy of
+        // tile t+2 into the buffer of tile t-1, which every wave finished before this
+        // barrier. Copies are thus requested two tiles ahead.
+        issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, 0, 0, lK[0], lV[0], wave);
+        if (n_kt > 1) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, tk, tv, lK[1], lV[1], wave);
         for (int g = 0; 3 * g < n_kt; ++g) {
 #pragma unroll
             for (int u = 0; u < 3; ++u) {
                 const int t = 3 * g + u;
                 if (t >= n_kt) break;
-                __syncthreads();
-                if (t + 1 < n_kt)
-                    issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, (t + 1) * tk, (t + 1) * tv,
-                                   lK[(u + 1) % 3], lV[(u + 1) % 3], wave);
+                if (t + 1 < n_kt) {      // the copy of tile t+1 may stay outstanding
+                    if constexpr (NI == 2) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                    else asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+                }
+                if (t + 2 < n_kt)
+                    issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, (t + 2) * tk, (t + 2) * tv,
+                                   lK[(u + 2) % 3], lV[(u + 2) % 3], wave);
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const int i = 2 * t + half;
@@ -482,9 +571,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                 qk(i + 1, cKb[kb], s_nxt, la);
                 pv(i - 1, cVb[vbuf], p_prev, la);
                 softmax(s_cur, p_cur, st);
-#ifndef AULE_NO_INTERLEAVE
                 interleave();
-#endif
             } else {
                 pv(i - 1, cVb[vbuf], p_prev, la);
                 softmax(s_cur, p_cur, st);
@@ -507,7 +594,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         const int lb = (last / 2) % 3;
         pv(last, lb == 0 ? cVb[0] : lb == 1 ? cVb[1] : cVb[2], p_prev, lane_addr(lane));
     }
-    }  // PIPE
+    }  // loop forms
 
     // ---------------------------------------------------------------- epilogue
 #pragma unroll
@@ -535,44 +622,58 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 
 int heads_per_group(int group) { return (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1; }
 
-int mfma_shape() {
+int mfma_loop() {
     static const int v = [] {
-        const char* e = std::getenv("AULE_MFMA_SHAPE");
+        const char* e = std::getenv("AULE_MFMA_LOOP");
         const int v = e ? std::atoi(e) : 0;
-        return (v >= 0 && v <= 1) ? v : 0;
+        return (v >= 0 && v <= 2) ? v : 0;
+    }();
+    return v;
+}
+// which wave-index bit splits the ping-pong groups (waves w and w+4 share a SIMD: bit 2)
+int pp_shift() {
+    static const int v = [] {
+        const char* e = std::getenv("AULE_PP_SHIFT");
+        const int v = e ? std::atoi(e) : 2;
+        return (v >= 0 && v <= 2) ? v : 2;
     }();
     return v;
 }
 
-template <typename T, int D, int WAVES, int NB, int GH, bool PIPE, bool CAUSAL, bool VARLEN>
+template <typename T, int D, int WAVES, int NB, int GH, int LOOP, bool CAUSAL, bool VARLEN>
 hipError_t launch_cfg(const AttnProblem& p, hipStream_t stream) {
     constexpr int BMW = 32 * NB * (WAVES / GH);
     dim3 block(WAVES * 64);
+    AttnProblem pp = p;
+    pp.pp_shift = pp_shift();
     if constexpr (VARLEN) {
         dim3 grid(varlen_grid_tiles(p.total_tokens, p.batch, BMW), p.heads_q / GH, 1);
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, PIPE, CAUSAL, true>), grid, block, 0, stream, p, 0);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, LOOP, CAUSAL, true>), grid, block, 0, stream, pp, 0);
     } else {
         const int n_qtiles = (p.seqlen_q + BMW - 1) / BMW;
         const int64_t nblocks = (int64_t)n_qtiles * p.batch * (p.heads_q / GH);
         if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
         dim3 grid((unsigned)nblocks);
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, PIPE, CAUSAL, false>), grid, block, 0, stream, p, n_qtiles);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, LOOP, CAUSAL, false>), grid, block, 0, stream, pp, n_qtiles);
     }
     return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_gh(const AttnProblem& p, hipStream_t stream) {
-    // kernel shape: 8 waves x 32 rows; AULE_MFMA_SHAPE=1 selects the software-pipelined
-    // loop instead of the straight one
+    // loop form: AULE_MFMA_LOOP=0 straight (default), 1 software-pipelined, 2 ping-pong
     const int gh = VARLEN ? 1 : heads_per_group(p.group);
-    switch ((mfma_shape() == 1 ? 3 : 0) + (gh == 4 ? 2 : gh == 2 ? 1 : 0)) {
-        case 0: return launch_cfg<T, D, 8, 1, 1, false, CAUSAL, VARLEN>(p, stream);
-        case 1: return launch_cfg<T, D, 8, 1, 2, false, CAUSAL, VARLEN>(p, stream);
-        case 2: return launch_cfg<T, D, 8, 1, 4, false, CAUSAL, VARLEN>(p, stream);
-        case 3: return launch_cfg<T, D, 8, 1, 1, true, CAUSAL, VARLEN>(p, stream);
-        case 4: return launch_cfg<T, D, 8, 1, 2, true, CAUSAL, VARLEN>(p, stream);
-        case 5: return launch_cfg<T, D, 8, 1, 4, true, CAUSAL, VARLEN>(p, stream);
+    const int g = gh == 4 ? 2 : gh == 2 ? 1 : 0;
+    switch (mfma_loop() * 3 + g) {
+        case 0: return launch_cfg<T, D, 8, 1, 1, 0, CAUSAL, VARLEN>(p, stream);
+        case 1: return launch_cfg<T, D, 8, 1, 2, 0, CAUSAL, VARLEN>(p, stream);
+        case 2: return launch_cfg<T, D, 8, 1, 4, 0, CAUSAL, VARLEN>(p, stream);
+        case 3: return launch_cfg<T, D, 8, 1, 1, 1, CAUSAL, VARLEN>(p, stream);
+        case 4: return launch_cfg<T, D, 8, 1, 2, 1, CAUSAL, VARLEN>(p, stream);
+        case 5: return launch_cfg<T, D, 8, 1, 4, 1, CAUSAL, VARLEN>(p, stream);
+        case 6: return launch_cfg<T, D, 8, 1, 1, 2, CAUSAL, VARLEN>(p, stream);
+        case 7: return launch_cfg<T, D, 8, 1, 2, 2, CAUSAL, VARLEN>(p, stream);
+        case 8: return launch_cfg<T, D, 8, 1, 4, 2, CAUSAL, VARLEN>(p, stream);
     }
     return hipErrorInvalidValue;
 }
