@@ -50,6 +50,7 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -58,8 +59,14 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBN = 64;               // keys per K/V tile (two 32-key sub-steps)
 [[maybe_unused]] constexpr float kRescaleSlack = 8.0f; // log2 units
+[[maybe_unused]] constexpr float kSlackExp = 256.0f;   // 2^kRescaleSlack
+#ifndef AULE_DMA_PARTS
+#define AULE_DMA_PARTS 4
+#endif
+#ifndef AULE_SOFTMAX_FAST
+#define AULE_SOFTMAX_FAST 1
+#endif
 
 template <typename T> struct Mfma;
 template <> struct Mfma<bf16_t> {
@@ -115,20 +122,61 @@ template <int KC> __device__ __forceinline__ int vswz(int row) {
 [[maybe_unused]] constexpr uint32_t kOobOffset = 0x7FFFFFF0u;     // an offset past any slice: reads as zero
 
 #if defined(__HIP_DEVICE_COMPILE__)
-// Start the global -> LDS copy of K/V tile j: NI 16-byte loads per lane for each of K and
+// One 16-byte global -> LDS copy per lane: LDS[m0 + 16 * lane] = buffer[voffset], zero when
+// voffset lies past the descriptor's size. Written as inline asm so the compiler does not
+// track it: its alias analysis cannot tell the destination buffer from the buffers being
+// read and would otherwise wait for every copy right after issuing it. Completion is
+// ordered explicitly instead (s_waitcnt vmcnt + s_barrier at tile boundaries). M0 is saved
+// and restored around the copy.
+__device__ __forceinline__ void lds_copy16(i32x4 rsrc, uint32_t voffset, uint32_t lds_addr) {
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(voffset), "s"(rsrc), "s"(lds_addr));
+}
+
+// Raw buffer descriptor (stride 0, bounds-checked by num_records bytes).
+__device__ __forceinline__ i32x4 buffer_desc(const void* base, int num_records) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), num_records, (int)kBufferFlags};
+}
+
+// Start the global -> LDS copy of one K/V tile: NI 16-byte loads per lane for each of K and
 // V; wave w fills LDS chunk slots [(w*NI + i) * 64, +64) of the tile buffers.
 template <int NI>
-__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                           const uint32_t (&koff)[NI], const uint32_t (&voff)[NI],
-                                           uint32_t tile_k_bytes, uint32_t tile_v_bytes,
-                                           lds_void* dK, lds_void* dV, int wave) {
+__device__ __forceinline__ void issue_tile(i32x4 rk, i32x4 rv, const uint32_t (&koff)[NI],
+                                           const uint32_t (&voff)[NI], uint32_t tile_k_bytes,
+                                           uint32_t tile_v_bytes, uint32_t dK, uint32_t dV, int wave) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int slot = (wave * NI + i) * 64 * 16;   // bytes
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)((__attribute__((address_space(3))) char*)dK + slot),
-                                                 16, koff[i] + tile_k_bytes, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)((__attribute__((address_space(3))) char*)dV + slot),
-                                                 16, voff[i] + tile_v_bytes, 0, 0, 0);
+        const uint32_t slot = (uint32_t)(wave * NI + i) * 64u * 16u;   // bytes
+        lds_copy16(rk, koff[i] + tile_k_bytes, __builtin_amdgcn_readfirstlane(dK + slot));
+        lds_copy16(rv, voff[i] + tile_v_bytes, __builtin_amdgcn_readfirstlane(dV + slot));
+    }
+}
+// Part `part` of `parts` of the same copy: instructions [part * 2NI / parts, ...) of the
+// 2NI (K first, then V). Spreading a tile's copy over several calls keeps a wave from
+// stalling on a long run of copy instructions, which issue in order behind every other
+// wave's copies.
+template <int NI, int PARTS>
+__device__ __forceinline__ void issue_tile_part(int part, i32x4 rk, i32x4 rv, const uint32_t (&koff)[NI],
+                                                const uint32_t (&voff)[NI], uint32_t tile_k_bytes,
+                                                uint32_t tile_v_bytes, uint32_t dK, uint32_t dV, int wave) {
+    constexpr int PER = 2 * NI / PARTS;
+    static_assert(PER * PARTS == 2 * NI, "copy parts must split the tile evenly");
+#pragma unroll
+    for (int j = 0; j < 2 * NI; ++j) {
+        if (j / PER != part) continue;
+        const int i = j % NI;
+        const uint32_t slot = (uint32_t)(wave * NI + i) * 64u * 16u;   // bytes
+        if (j < NI) lds_copy16(rk, koff[i] + tile_k_bytes, __builtin_amdgcn_readfirstlane(dK + slot));
+        else lds_copy16(rv, voff[i] + tile_v_bytes, __builtin_amdgcn_readfirstlane(dV + slot));
     }
 }
 #endif  // __HIP_DEVICE_COMPILE__
@@ -136,7 +184,16 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_b
 // WAVES waves per workgroup (4: one per SIMD, 8: two per SIMD so one wave's softmax runs
 // while the other's matrix products do); each wave owns NB blocks of 32 query rows of one
 // query head.
-template <typename T, int D, int WAVES, int NB, int GH, int LOOP, bool CAUSAL, bool VARLEN>
+// Wait until at most N of this wave's vector-memory operations are outstanding and for its
+// LDS reads, then join the workgroup barrier.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+}
+
+// TB: keys per K/V tile (64: three LDS buffers, copies requested two tiles ahead;
+// 128: two buffers, one tile ahead).
+template <typename T, int D, int WAVES, int NB, int GH, int TB, int LOOP, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WAVES / 4)))
 void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -147,12 +204,19 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     constexpr int KC = D / 8;                    // 16-byte chunks per K / V row
     constexpr int KS = D / 16;                   // k-steps of S^T = K Q^T
     constexpr int DB = D / 32;                   // 32-row d-blocks of O^T
+    constexpr int kBN = TB;                      // keys per K/V tile
+    constexpr int SPT = TB / 32;                 // 32-key sub-steps per tile
+    constexpr int NBUF = TB == 64 ? 3 : 2;       // LDS tile buffers
+    constexpr int AHEAD = NBUF - 1;              // tiles requested ahead
+    constexpr int DMA_PARTS = AULE_DMA_PARTS < SPT ? AULE_DMA_PARTS : SPT;   // pieces of a tile copy
+    static_assert(TB == 64 || TB == 128, "tile of 64 or 128 keys");
+    static_assert(LOOP != 2 || TB == 64, "the ping-pong loop uses 64-key tiles");
     constexpr int TILE_CHUNKS = kBN * KC;        // 16-byte chunks per K (or V) tile
     constexpr int NI = TILE_CHUNKS / kThreads;   // load instructions per wave per tile
     static_assert(NI >= 1 && TILE_CHUNKS % kThreads == 0, "tile must split evenly over the waves");
 
-    __shared__ u32x4 sK0[TILE_CHUNKS], sK1[TILE_CHUNKS], sK2[TILE_CHUNKS];
-    __shared__ u32x4 sV0[TILE_CHUNKS], sV1[TILE_CHUNKS], sV2[TILE_CHUNKS];
+    __shared__ u32x4 sK[NBUF][TILE_CHUNKS];
+    __shared__ u32x4 sV[NBUF][TILE_CHUNKS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -205,8 +269,8 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     const uint32_t v_rs = (uint32_t)(p.v_rstride * (int64_t)sizeof(T));
     const int k_valid = Lk > 0 ? (int)((int64_t)(Lk - 1) * k_rs + hd * sizeof(T)) : 0;
     const int v_valid = Lk > 0 ? (int)((int64_t)(Lk - 1) * v_rs + hd * sizeof(T)) : 0;
-    const __amdgpu_buffer_rsrc_t rsrc_k = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(kb), 0, k_valid, kBufferFlags);
-    const __amdgpu_buffer_rsrc_t rsrc_v = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(vb), 0, v_valid, kBufferFlags);
+    const i32x4 rsrc_k = buffer_desc(kb, k_valid);
+    const i32x4 rsrc_v = buffer_desc(vb, v_valid);
     // Per-lane byte offsets (tile-relative) of the global chunk that lands in this lane's
     // LDS slot, for each of the NI load instructions of this wave.
     uint32_t koff[NI], voff[NI];
@@ -242,7 +306,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     const int wg_rows_end = min(tile * BMW + BMW, Lq);
     const int keys_needed = CAUSAL ? wg_rows_end : Lk;
     const int nsub = (keys_needed + 31) / 32;
-    const int n_kt = (nsub + 1) / 2;
+    const int n_kt = (nsub + SPT - 1) / SPT;
 
     // ---------------------------------------------------------------- accumulators
     f32x16 o[DB][NB];
@@ -271,32 +335,20 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         return a;
     };
 
-    // S^T = K Q^T for sub-step `sub` (32 keys x 32*NB queries) from K tile buffer cK
-    auto qk = [&](int sub, const u32x4* cK, f32x16 (&acc)[NB], const LaneAddr& la) {
+    // K fragments of sub-step `sub` (A operands of S^T = K Q^T, rows in sigma order)
+    auto load_k = [&](int sub, const u32x4* cK, const LaneAddr& la, u32x4 (&kf)[KS]) {
+        const int krow = 32 * (sub % SPT) + la.krow_sig;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) kf[ks] = cK[krow * KC + ((2 * ks + la.h) ^ la.kx)];
+    };
+    // S^T = K Q^T: 32 keys x 32*NB queries
+    auto mma_qk = [&](const u32x4 (&kf)[KS], f32x16 (&acc)[NB]) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x16{};
-        const int krow = 32 * (sub & 1) + la.krow_sig;
-#if defined(AULE_QK_PREFETCH)
-        u32x4 af[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) af[ks] = cK[krow * KC + ((2 * ks + la.h) ^ la.kx)];
-#endif
-#if defined(AULE_SETPRIO)
-        __builtin_amdgcn_s_setprio(1);
-#endif
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-#if defined(AULE_QK_PREFETCH)
-            const u32x4 a = af[ks];
-#else
-            const u32x4 a = cK[krow * KC + ((2 * ks + la.h) ^ la.kx)];
-#endif
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[nb] = Mfma<T>::mma(a, qf[nb][ks], acc[nb]);
-        }
-#if defined(AULE_SETPRIO)
-        __builtin_amdgcn_s_setprio(0);
-#endif
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = Mfma<T>::mma(kf[ks], qf[nb][ks], acc[nb]);
     };
     // -inf for keys past the end and (causal) keys after the query; a uniform branch
     auto mask = [&](int sub, f32x16 (&acc)[NB]) {
@@ -314,39 +366,95 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
             }
         }
     };
-    // O^T += V^T P^T for sub-step `sub` from V tile buffer cV
-    auto pv = [&](int sub, const u32x4* cV, const u32x4 (&pf)[2][NB], const LaneAddr& la) {
-#if defined(AULE_SETPRIO)
-        __builtin_amdgcn_s_setprio(1);
-#endif
+    // V^T fragments of sub-step `sub` (A operands of O^T = V^T P^T): two transposed 8-byte
+    // reads per 16-key chunk and 32-row d-block
+    auto load_v = [&](int sub, const u32x4* cV, const LaneAddr& la, u32x4 (&vf)[2][DB]) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-            const int kc = 2 * (sub & 1) + cc;
+            const int kc = 2 * (sub % SPT) + cc;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                u32x4 a;
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int key = 16 * kc + 4 * t + la.tv_key;
                     const char* addr = reinterpret_cast<const char*>(cV + key * KC + ((4 * db + la.tv_chunk) ^ la.tv_swz)) + la.tv_within;
                     const i16x4_t part = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<char*>(addr)));
                     const u32x2 w = __builtin_bit_cast(u32x2, part);
-                    a[2 * t] = w[0];
-                    a[2 * t + 1] = w[1];
+                    vf[cc][db][2 * t] = w[0];
+                    vf[cc][db][2 * t + 1] = w[1];
                 }
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) o[db][nb] = Mfma<T>::mma(a, pf[cc][nb], o[db][nb]);
             }
         }
-#if defined(AULE_SETPRIO)
-        __builtin_amdgcn_s_setprio(0);
-#endif
+    };
+    // O^T += V^T P^T over one sub-step
+    auto mma_pv = [&](const u32x4 (&vf)[2][DB], const u32x4 (&pf)[2][NB]) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) o[db][nb] = Mfma<T>::mma(vf[cc][db], pf[cc][nb], o[db][nb]);
+    };
+    auto qk = [&](int sub, const u32x4* cK, f32x16 (&acc)[NB], const LaneAddr& la) {
+        u32x4 kf[KS];
+        load_k(sub, cK, la, kf);
+        mma_qk(kf, acc);
+    };
+    auto pv = [&](int sub, const u32x4* cV, const u32x4 (&pf)[2][NB], const LaneAddr& la) {
+        u32x4 vf[2][DB];
+        load_v(sub, cV, la, vf);
+        mma_pv(vf, pf);
     };
     // online softmax of one sub-step: P (packed 16-bit) relative to the possibly raised
     // reference max; the O / l rescale is applied by finish() after this sub-step's
     // neighbours in the pipeline have been issued
     struct Soft { float m_new[NB], alpha[NB], lsum[NB]; bool raise[NB]; };
+    // P = exp2(s * c - m) packed to 16 bit, with its row sum over the rounded values
+    auto exp_pack = [&](const f32x16& a, float m, u32x4 (&pf)[2][NB], int nb) {
+        const float mneg = -m;
+        float lsum = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            float pv8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pv8[e] = __builtin_amdgcn_exp2f(fmaf(a[8 * cc + e], c, mneg));
+            const u32x4 pk = {Mfma<T>::pack2(pv8[0], pv8[1]), Mfma<T>::pack2(pv8[2], pv8[3]),
+                              Mfma<T>::pack2(pv8[4], pv8[5]), Mfma<T>::pack2(pv8[6], pv8[7])};
+            // the row sum uses the same rounded P that multiplies V, so O stays an exact
+            // convex combination of V rows up to fp32 accumulation
+#pragma unroll
+            for (int w = 0; w < 4; ++w) lsum = Mfma<T>::sum2(pk[w], lsum);
+            pf[cc][nb] = pk;
+        }
+        return lsum;
+    };
     auto softmax = [&](const f32x16 (&acc)[NB], u32x4 (&pf)[2][NB], Soft& st) {
+#if AULE_SOFTMAX_FAST
+        // Fast path: exponentiate against the current reference max right away. If no
+        // lane's partial row sum exceeds 2^slack, no single P does, so no score exceeds the
+        // reference by more than the slack and the full path below would keep the reference
+        // too (up to rounding exactly at the threshold, where either choice keeps P in
+        // range): same P and sums, without the row max. Otherwise (and on the first
+        // sub-step, where the reference is -inf and the sums are inf or NaN) the full path
+        // recomputes everything.
+        {
+            bool ok = true;
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                st.lsum[nb] = exp_pack(acc[nb], m_ref[nb], pf, nb);
+                ok = ok && (st.lsum[nb] <= kSlackExp);
+            }
+            if (__all(ok)) {
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+                    st.raise[nb] = false;
+                    st.m_new[nb] = m_ref[nb];
+                    st.alpha[nb] = 1.f;
+                }
+                return;
+            }
+        }
+#endif
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             float mx = -INFINITY;
@@ -359,22 +467,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
             st.raise[nb] = any;
             st.m_new[nb] = m_new;
             st.alpha[nb] = __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
-            const float mneg = -m_new;
-            float lsum = 0.f;
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                float pv8[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pv8[e] = __builtin_amdgcn_exp2f(fmaf(acc[nb][8 * cc + e], c, mneg));
-                const u32x4 pk = {Mfma<T>::pack2(pv8[0], pv8[1]), Mfma<T>::pack2(pv8[2], pv8[3]),
-                                  Mfma<T>::pack2(pv8[4], pv8[5]), Mfma<T>::pack2(pv8[6], pv8[7])};
-                // the row sum uses the same rounded P that multiplies V, so O stays an
-                // exact convex combination of V rows up to fp32 accumulation
-#pragma unroll
-                for (int w = 0; w < 4; ++w) lsum = Mfma<T>::sum2(pk[w], lsum);
-                pf[cc][nb] = pk;
-            }
-            st.lsum[nb] = lsum;
+            st.lsum[nb] = exp_pack(acc[nb], m_new, pf, nb);
         }
     };
     auto finish = [&](const Soft& st) {
@@ -390,22 +483,25 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         }
     };
 
-    // ---------------------------------------------------------------- pipelined main loop
-    // Iteration i issues, in one basic block, the matrix products of S(i+1) = K Q^T and of
-    // O += V^T P(i-1) together with the softmax of S(i), so the vector ALU work of one
-    // sub-step overlaps the matrix-core work of its neighbours. K/V tiles are triple
-    // buffered (tile t in buffer t % 3): the copy of tile t+1 starts at the barrier before
-    // the first iteration that reads tile t and must land by the next such barrier, one
-    // tile later; by then tile t-2, which shared its buffer, has been read for the last
-    // time. Iterations are unrolled by six so every buffer choice is a compile-time one.
+    // ---------------------------------------------------------------- main loop
+    // K/V tiles are triple buffered (tile t in buffer t % 3). Every buffer choice is a
+    // compile-time one after unrolling, and every tile-copy completion is ordered by an
+    // explicit s_waitcnt vmcnt + s_barrier (the copies are invisible to the compiler).
     const uint32_t tk = kBN * k_rs, tv = kBN * v_rs;   // bytes per K / V tile
-    lds_void* const lK[3] = {(lds_void*)sK0, (lds_void*)sK1, (lds_void*)sK2};
-    lds_void* const lV[3] = {(lds_void*)sV0, (lds_void*)sV1, (lds_void*)sV2};
-    const u32x4* const cKb[3] = {sK0, sK1, sK2};
-    const u32x4* const cVb[3] = {sV0, sV1, sV2};
+    auto lds_off = [](const u32x4* p) { return (uint32_t)(uintptr_t)(lds_void*)p; };
+    uint32_t lK[NBUF], lV[NBUF];
+    const u32x4* cKb[NBUF];
+    const u32x4* cVb[NBUF];
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) {
+        lK[b] = lds_off(sK[b]);
+        lV[b] = lds_off(sV[b]);
+        cKb[b] = sK[b];
+        cVb[b] = sV[b];
+    }
 
-    f32x16 s_cur[NB], s_nxt[NB];
-    u32x4 p_prev[2][NB], p_cur[2][NB];
+    f32x16 s_cur[NB];
+    u32x4 p_cur[2][NB];
 
     if constexpr (LOOP == 2) {
         // Ping-pong: the two waves of a SIMD (groups 0 and 1) alternate between a matrix
@@ -421,12 +517,8 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         u32x4 pb[2][NB];
         auto phase_barrier = [&](bool wait_tile, bool newer_pending) {
             if (wait_tile) {
-                if (newer_pending) {
-                    if constexpr (NI == 2) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                    else asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                } else {
-                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                }
+                if (newer_pending) wait_vmcnt_barrier<2 * NI>();
+                else wait_vmcnt_barrier<0>();
             } else {
                 asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             }
@@ -469,132 +561,108 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         }
     } else if constexpr (LOOP == 0) {
         // Straight loop: per 32-key sub-step S = K Q^T, mask, softmax, P V. Tile t sits in
-        // buffer t % 3. At the barrier before tile t each wave waits only for its copy of
-        // tile t (the copy of tile t+1 may still be in flight), then starts the copy of
-        // tile t+2 into the buffer of tile t-1, which every wave finished before this
-        // barrier. Copies are thus requested two tiles ahead.
-        issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, 0, 0, lK[0], lV[0], wave);
-        if (n_kt > 1) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, tk, tv, lK[1], lV[1], wave);
-        for (int g = 0; 3 * g < n_kt; ++g) {
+        // buffer t % NBUF. At the barrier before tile t each wave waits only for its copy
+        // of tile t (newer copies may stay in flight), then starts the copy of tile
+        // t + AHEAD into the buffer of tile t-1, which every wave finished before this
+        // barrier.
 #pragma unroll
-            for (int u = 0; u < 3; ++u) {
-                const int t = 3 * g + u;
+        for (int a = 0; a < AHEAD; ++a)
+            if (a < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, a * tk, a * tv, lK[a], lV[a], wave);
+        for (int g = 0; NBUF * g < n_kt; ++g) {
+#pragma unroll
+            for (int u = 0; u < NBUF; ++u) {
+                const int t = NBUF * g + u;
                 if (t >= n_kt) break;
-                if (t + 1 < n_kt) {      // the copy of tile t+1 may stay outstanding
-                    if constexpr (NI == 2) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                    else asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                } else {
-                    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-                }
-                if (t + 2 < n_kt)
-                    issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, (t + 2) * tk, (t + 2) * tv,
-                                   lK[(u + 2) % 3], lV[(u + 2) % 3], wave);
+                if (AHEAD == 2 && t + 1 < n_kt) wait_vmcnt_barrier<2 * NI>();   // tile t+1 may stay in flight
+                else wait_vmcnt_barrier<0>();
+                // Fragment reads run one step ahead of their use: after the S^T products of
+                // sub-step i are issued, the V fragments of i and the K fragments of i+1 are
+                // requested, and arrive while the softmax of i runs. The copy of tile
+                // t + AHEAD is issued in DMA_PARTS pieces, one after each of the first
+                // DMA_PARTS sub-steps' S^T products (every sub-step of a tile that is not the
+                // last one runs, so all pieces are issued before the next barrier).
+                const LaneAddr la = lane_addr(lane);
+                u32x4 kf[KS];
+                u32x4 vf[2][DB];
+                load_k(SPT * t, cKb[u], la, kf);
+                const bool copy_next = t + AHEAD < n_kt;
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int i = 2 * t + half;
+                for (int h = 0; h < SPT; ++h) {
+                    const int i = SPT * t + h;
                     if (i >= nsub) break;
-                    const LaneAddr la = lane_addr(lane);
-                    qk(i, cKb[u], s_cur, la);
+                    mma_qk(kf, s_cur);
+                    if (h < DMA_PARTS && copy_next)
+                        issue_tile_part<NI, DMA_PARTS>(h, rsrc_k, rsrc_v, koff, voff, (t + AHEAD) * tk, (t + AHEAD) * tv,
+                                                       lK[(u + AHEAD) % NBUF], lV[(u + AHEAD) % NBUF], wave);
+                    load_v(i, cVb[u], la, vf);
+                    if (h + 1 < SPT) load_k(i + 1, cKb[u], la, kf);
                     mask(i, s_cur);
                     Soft st;
                     softmax(s_cur, p_cur, st);
                     finish(st);
-                    pv(i, cVb[u], p_cur, la);
+                    mma_pv(vf, p_cur);
+                }
+            }
+        }
+    } else if constexpr (LOOP == 3) {
+        // Straight tiles with the sub-steps pipelined inside each wave: the S^T products of
+        // sub-step i+1 are issued interleaved with the softmax of sub-step i (one matrix
+        // instruction, then a slice of vector work), so a wave keeps the matrix unit fed
+        // while it exponentiates. V fragments are read after the K fragments are dead, to
+        // stay within the register budget of two waves per SIMD.
+#pragma unroll
+        for (int a = 0; a < AHEAD; ++a)
+            if (a < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, a * tk, a * tv, lK[a], lV[a], wave);
+        for (int g = 0; NBUF * g < n_kt; ++g) {
+#pragma unroll
+            for (int u = 0; u < NBUF; ++u) {
+                const int t = NBUF * g + u;
+                if (t >= n_kt) break;
+                if (AHEAD == 2 && t + 1 < n_kt) wait_vmcnt_barrier<2 * NI>();
+                else wait_vmcnt_barrier<0>();
+                const bool copy_next = t + AHEAD < n_kt;
+                const LaneAddr la = lane_addr(lane);
+                const int i0 = SPT * t;
+                {
+                    u32x4 kf[KS];
+                    load_k(i0, cKb[u], la, kf);
+                    mma_qk(kf, s_cur);
+                }
+#pragma unroll
+                for (int h = 0; h < SPT; ++h) {
+                    const int i = i0 + h;
+                    if (i >= nsub) break;
+                    if (h < DMA_PARTS && copy_next)
+                        issue_tile_part<NI, DMA_PARTS>(h, rsrc_k, rsrc_v, koff, voff, (t + AHEAD) * tk, (t + AHEAD) * tv,
+                                                       lK[(u + AHEAD) % NBUF], lV[(u + AHEAD) % NBUF], wave);
+                    mask(i, s_cur);
+                    const bool more = (h + 1 < SPT) && (i + 1 < nsub);
+                    f32x16 s_nxt[NB];
+                    Soft st;
+                    if (more) {
+                        u32x4 kf[KS];
+                        load_k(i + 1, cKb[u], la, kf);
+                        mma_qk(kf, s_nxt);
+                        softmax(s_cur, p_cur, st);
+                    } else {
+                        softmax(s_cur, p_cur, st);
+                    }
+                    finish(st);
+                    {
+                        u32x4 vf[2][DB];
+                        load_v(i, cVb[u], la, vf);
+                        mma_pv(vf, p_cur);
+                    }
+                    if (more) {
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) s_cur[nb] = s_nxt[nb];
+                    }
                 }
             }
         }
     } else {
-
-    // Instruction order of a full iteration (one basic block): a few LDS fragment reads up
-    // front, then groups of one MFMA, a slice of the softmax VALU work and the next LDS
-    // reads, so the matrix core and the vector ALU stay busy together and the fragment
-    // registers stay short-lived.
-    auto interleave = [&]() {
-        constexpr int kMfma = NB * (KS + 2 * DB);      // matrix products per iteration
-        constexpr int kDs = KS + 4 * DB;               // LDS fragment reads per iteration
-        constexpr int kValu = (48 * NB + 32 + kMfma - 1) / kMfma;
-        constexpr int kDsPer = (kDs - 4 + kMfma - 1) / kMfma;
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-        for (int k = 0; k < kMfma; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, kDsPer, 0);
-        }
-    };
-
-    issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, 0, 0, lK[0], lV[0], wave);
-    __syncthreads();
-    if (n_kt > 1) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, tk, tv, lK[1], lV[1], wave);
-    qk(0, cKb[0], s_cur, lane_addr(lane));
-    mask(0, s_cur);
-    {
-        Soft st;
-        if (nsub > 1) {
-            qk(1, cKb[0], s_nxt, lane_addr(lane));
-            softmax(s_cur, p_cur, st);
-        } else {
-            softmax(s_cur, p_cur, st);
-        }
-        finish(st);
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) p_prev[cc][nb] = p_cur[cc][nb];
-        if (nsub > 1) {
-            mask(1, s_nxt);
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) s_cur[nb] = s_nxt[nb];
-        }
+        static_assert(LOOP == 0 || LOOP == 2 || LOOP == 3, "loop form");
     }
-    for (int g = 0; 6 * g + 1 < nsub; ++g) {
-#pragma unroll
-        for (int u = 1; u <= 6; ++u) {
-            const int i = 6 * g + u;
-            if (i >= nsub) break;
-            const int kb = ((u + 1) / 2) % 3;     // buffer of tile (i+1)/2
-            const int vbuf = ((u - 1) / 2) % 3;   // buffer of tile (i-1)/2
-            if (u & 1) {
-                const int t = (i + 1) / 2;         // first iteration that reads tile t
-                if (t < n_kt) {
-                    __syncthreads();               // tile t landed; tile t-2 fully read
-                    if (t + 1 < n_kt)
-                        issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, (t + 1) * tk, (t + 1) * tv,
-                                       lK[(kb + 1) % 3], lV[(kb + 1) % 3], wave);
-                }
-            }
-            int lane_o = lane;
-            asm volatile("" : "+v"(lane_o));
-            const LaneAddr la = lane_addr(lane_o);
-            Soft st;
-            if (i + 1 < nsub) {
-                qk(i + 1, cKb[kb], s_nxt, la);
-                pv(i - 1, cVb[vbuf], p_prev, la);
-                softmax(s_cur, p_cur, st);
-                interleave();
-            } else {
-                pv(i - 1, cVb[vbuf], p_prev, la);
-                softmax(s_cur, p_cur, st);
-            }
-            finish(st);
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) p_prev[cc][nb] = p_cur[cc][nb];
-            if (i + 1 < nsub) {
-                mask(i + 1, s_nxt);
-#pragma unroll
-                for (int nb = 0; nb < NB; ++nb) s_cur[nb] = s_nxt[nb];
-            }
-        }
-    }
-    // the last sub-step's P^T V
-    {
-        const int last = nsub - 1;
-        const int lb = (last / 2) % 3;
-        pv(last, lb == 0 ? cVb[0] : lb == 1 ? cVb[1] : cVb[2], p_prev, lane_addr(lane));
-    }
-    }  // loop forms
 
     // ---------------------------------------------------------------- epilogue
 #pragma unroll
@@ -625,8 +693,8 @@ int heads_per_group(int group) { return (group % 4 == 0) ? 4 : (group % 2 == 0) 
 int mfma_loop() {
     static const int v = [] {
         const char* e = std::getenv("AULE_MFMA_LOOP");
-        const int v = e ? std::atoi(e) : 0;
-        return (v >= 0 && v <= 2) ? v : 0;
+        const int v = e ? std::atoi(e) : 1;
+        return (v >= 0 && v <= 3) ? v : 1;
     }();
     return v;
 }
@@ -640,7 +708,7 @@ int pp_shift() {
     return v;
 }
 
-template <typename T, int D, int WAVES, int NB, int GH, int LOOP, bool CAUSAL, bool VARLEN>
+template <typename T, int D, int WAVES, int NB, int GH, int TB, int LOOP, bool CAUSAL, bool VARLEN>
 hipError_t launch_cfg(const AttnProblem& p, hipStream_t stream) {
     constexpr int BMW = 32 * NB * (WAVES / GH);
     dim3 block(WAVES * 64);
@@ -648,32 +716,36 @@ hipError_t launch_cfg(const AttnProblem& p, hipStream_t stream) {
     pp.pp_shift = pp_shift();
     if constexpr (VARLEN) {
         dim3 grid(varlen_grid_tiles(p.total_tokens, p.batch, BMW), p.heads_q / GH, 1);
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, LOOP, CAUSAL, true>), grid, block, 0, stream, pp, 0);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, TB, LOOP, CAUSAL, true>), grid, block, 0, stream, pp, 0);
     } else {
         const int n_qtiles = (p.seqlen_q + BMW - 1) / BMW;
         const int64_t nblocks = (int64_t)n_qtiles * p.batch * (p.heads_q / GH);
         if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
         dim3 grid((unsigned)nblocks);
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, LOOP, CAUSAL, false>), grid, block, 0, stream, pp, n_qtiles);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, TB, LOOP, CAUSAL, false>), grid, block, 0, stream, pp, n_qtiles);
     }
     return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_gh(const AttnProblem& p, hipStream_t stream) {
-    // loop form: AULE_MFMA_LOOP=0 straight (default), 1 software-pipelined, 2 ping-pong
+    // loop form (AULE_MFMA_LOOP): 0 straight with 64-key tiles, 1 straight with 128-key
+    // tiles (default), 2 ping-pong with 64-key tiles, 3 pipelined sub-steps with 128-key tiles
     const int gh = VARLEN ? 1 : heads_per_group(p.group);
     const int g = gh == 4 ? 2 : gh == 2 ? 1 : 0;
     switch (mfma_loop() * 3 + g) {
-        case 0: return launch_cfg<T, D, 8, 1, 1, 0, CAUSAL, VARLEN>(p, stream);
-        case 1: return launch_cfg<T, D, 8, 1, 2, 0, CAUSAL, VARLEN>(p, stream);
-        case 2: return launch_cfg<T, D, 8, 1, 4, 0, CAUSAL, VARLEN>(p, stream);
-        case 3: return launch_cfg<T, D, 8, 1, 1, 1, CAUSAL, VARLEN>(p, stream);
-        case 4: return launch_cfg<T, D, 8, 1, 2, 1, CAUSAL, VARLEN>(p, stream);
-        case 5: return launch_cfg<T, D, 8, 1, 4, 1, CAUSAL, VARLEN>(p, stream);
-        case 6: return launch_cfg<T, D, 8, 1, 1, 2, CAUSAL, VARLEN>(p, stream);
-        case 7: return launch_cfg<T, D, 8, 1, 2, 2, CAUSAL, VARLEN>(p, stream);
-        case 8: return launch_cfg<T, D, 8, 1, 4, 2, CAUSAL, VARLEN>(p, stream);
+        case 0: return launch_cfg<T, D, 8, 1, 1, 64, 0, CAUSAL, VARLEN>(p, stream);
+        case 1: return launch_cfg<T, D, 8, 1, 2, 64, 0, CAUSAL, VARLEN>(p, stream);
+        case 2: return launch_cfg<T, D, 8, 1, 4, 64, 0, CAUSAL, VARLEN>(p, stream);
+        case 3: return launch_cfg<T, D, 8, 1, 1, 128, 0, CAUSAL, VARLEN>(p, stream);
+        case 4: return launch_cfg<T, D, 8, 1, 2, 128, 0, CAUSAL, VARLEN>(p, stream);
+        case 5: return launch_cfg<T, D, 8, 1, 4, 128, 0, CAUSAL, VARLEN>(p, stream);
+        case 6: return launch_cfg<T, D, 8, 1, 1, 64, 2, CAUSAL, VARLEN>(p, stream);
+        case 7: return launch_cfg<T, D, 8, 1, 2, 64, 2, CAUSAL, VARLEN>(p, stream);
+        case 8: return launch_cfg<T, D, 8, 1, 4, 64, 2, CAUSAL, VARLEN>(p, stream);
+        case 9: return launch_cfg<T, D, 8, 1, 1, 128, 3, CAUSAL, VARLEN>(p, stream);
+        case 10: return launch_cfg<T, D, 8, 1, 2, 128, 3, CAUSAL, VARLEN>(p, stream);
+        case 11: return launch_cfg<T, D, 8, 1, 4, 128, 3, CAUSAL, VARLEN>(p, stream);
     }
     return hipErrorInvalidValue;
 }
