@@ -186,15 +186,27 @@ __device__ __forceinline__ void issue_tile_part(int part, i32x4 rk, i32x4 rv, co
 // query head.
 // Wait until at most N of this wave's vector-memory operations are outstanding and for its
 // LDS reads, then join the workgroup barrier.
+// The wait is issued through the builtin so that the compiler's own wait-count tracking
+// knows every LDS read has completed here (it cannot see waits inside inline asm and would
+// otherwise keep inserting conservative waits for reads that have long finished); the
+// barrier itself stays an asm statement with a memory clobber, which also keeps the
+// compiler from moving LDS accesses across it.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" :: "n"(N) : "memory");
+    static_assert(N >= 0 && N <= 63, "vmcnt field is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));   // vmcnt(N) lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+}
+// LDS reads done, then the workgroup barrier
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
 }
 
 // TB: keys per K/V tile (64: three LDS buffers, copies requested two tiles ahead;
 // 128: two buffers, one tile ahead).
 template <typename T, int D, int WAVES, int NB, int GH, int TB, int LOOP, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(WAVES / 4)))
+__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
     constexpr int kThreads = WAVES * 64;
@@ -206,7 +218,9 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     constexpr int DB = D / 32;                   // 32-row d-blocks of O^T
     constexpr int kBN = TB;                      // keys per K/V tile
     constexpr int SPT = TB / 32;                 // 32-key sub-steps per tile
-    constexpr int NBUF = TB == 64 ? 3 : 2;       // LDS tile buffers
+    // LDS tile buffers: 4 for the ping-pong; 3 for 64-key tiles in 8-wave workgroups; else 2
+    // (4-wave workgroups keep two workgroups per CU within the LDS)
+    constexpr int NBUF = LOOP == 2 ? 4 : (TB == 64 && WAVES == 8 ? 3 : 2);
     constexpr int AHEAD = NBUF - 1;              // tiles requested ahead
     constexpr int DMA_PARTS = AULE_DMA_PARTS < SPT ? AULE_DMA_PARTS : SPT;   // pieces of a tile copy
     static_assert(TB == 64 || TB == 128, "tile of 64 or 128 keys");
@@ -220,7 +234,9 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // wave-uniform (an SGPR): everything derived from it (rows, heads, ping-pong group,
+    // mask and barrier conditions) stays scalar, so those branches are scalar branches
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int ln = lane & 31;
 
@@ -283,21 +299,31 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         voff[i] = vdc * 8 < hd ? row * v_rs + vdc * 16 : kOobOffset;
     }
     // ---------------------------------------------------------------- Q -> registers
+    // Issued after the first K/V tile copies (load_q is called from each loop's prologue) so
+    // that both latencies overlap; a negative scale flips Q's sign bits in a separate
+    // uniform branch, which is the only place that waits for the loads before the loop.
     const bool neg = p.scale_log2 < 0.f;
     const float c = fmaxf(fabsf(p.scale_log2), 1e-30f);
     u32x4 qf[NB][KS];
+    auto load_q = [&]() {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const int row = qr0 + 32 * nb + ln;
+        for (int nb = 0; nb < NB; ++nb) {
+            const int row = qr0 + 32 * nb + ln;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int col = (2 * ks + h) * 8;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row < Lq && col < hd) v = *reinterpret_cast<const u32x4*>(qb + (int64_t)row * p.q_rstride + col);
-            if (neg) v ^= 0x80008000u;
-            qf[nb][ks] = v;
+            for (int ks = 0; ks < KS; ++ks) {
+                const int col = (2 * ks + h) * 8;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (row < Lq && col < hd) v = *reinterpret_cast<const u32x4*>(qb + (int64_t)row * p.q_rstride + col);
+                qf[nb][ks] = v;
+            }
         }
-    }
+        if (neg) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) qf[nb][ks] ^= 0x80008000u;
+        }
+    };
 
     // ---------------------------------------------------------------- sub-step ranges
     // The key range is walked in 32-key sub-steps; sub-steps 2t and 2t+1 live in K/V tile t.
@@ -504,59 +530,93 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     u32x4 p_cur[2][NB];
 
     if constexpr (LOOP == 2) {
-        // Ping-pong: the two waves of a SIMD (groups 0 and 1) alternate between a matrix
-        // block M_m = {O += V^T P(m-1), S(m) = K Q^T} and a softmax block V_v, with a
-        // workgroup barrier between phases. In phase p the group (p & 1) runs M_{p/2}
-        // while the other group runs V_{p/2 - 1 + (p & 1)}, so one wave's vector work
-        // hides under the other's matrix work. Tile t is read from phase 4t to phase 4t+5;
-        // with three buffers the copy of tile t+2 starts at phase 4t+2 (tile t-1, its
-        // buffer's previous tile, was last read in phase 4t+1) and is waited for at the
-        // barrier before phase 4(t+2), when only the copy of tile t+3 may be newer.
+        // Ping-pong. The two waves of a SIMD (group 0: wave bit p.pp_shift clear, group 1:
+        // set) alternate between a matrix phase M_m = {S(m) = K Q^T, O += V^T P(m-1)} that
+        // reads only registers, and a vector phase V_v = {mask and softmax of sub-step v;
+        // LDS reads of the K fragments of v+1 and the V fragments of v; one half of a tile
+        // copy}. Phases end at a workgroup barrier; in phase 2m group 0 runs M_m while group
+        // 1 runs V_{m-1}, in phase 2m+1 group 0 runs V_m while group 1 runs M_m, so each
+        // SIMD always has one wave issuing matrix instructions and one doing vector work.
+        //
+        // Tiles of 64 keys (sub-steps 2T, 2T+1) rotate through four LDS buffers. Tile T is
+        // first read in phase 4T-1 (group 0 prefetching K of sub-step 2T) and last read in
+        // phase 4T+4; its copy is issued in V_{2T-6} (K half) and V_{2T-5} (V half), after
+        // tile T-4 (same buffer) was last read in phase 4T-12, and waited for at the
+        // barrier that ends phase 4T-2, when each wave has issued at most the copy of tile
+        // T+1 and the K half of tile T+2 after it.
+        static_assert(NBUF == 4 && AHEAD == 3 && SPT == 2, "ping-pong schedule assumes 64-key tiles in 4 buffers");
         const int grp = (wave >> p.pp_shift) & 1;
-        f32x16 sb[NB];
-        u32x4 pb[2][NB];
-        auto phase_barrier = [&](bool wait_tile, bool newer_pending) {
-            if (wait_tile) {
-                if (newer_pending) wait_vmcnt_barrier<2 * NI>();
-                else wait_vmcnt_barrier<0>();
-            } else {
-                asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            }
+        u32x4 kf[KS];
+        u32x4 vf[2][DB];
+        auto copy_half = [&](int tile, int half, int buf) {
+            issue_tile_part<NI, 2>(half, rsrc_k, rsrc_v, koff, voff, tile * tk, tile * tv, lK[buf], lV[buf], wave);
         };
-        issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, 0, 0, lK[0], lV[0], wave);
-        if (n_kt > 1) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, tk, tv, lK[1], lV[1], wave);
-        phase_barrier(true, n_kt > 1);
-        const int nphase = 2 * nsub + 2;
-        for (int pg = 0; pg < nphase; pg += 12) {
+        auto wait_tile = [&](int tt) {   // at the barrier before phase 4tt-1
+            if (tt + 2 < n_kt) wait_vmcnt_barrier<3 * NI>();
+            else if (tt + 1 < n_kt) wait_vmcnt_barrier<2 * NI>();
+            else wait_vmcnt_barrier<0>();
+        };
+        auto phase_barrier = [&]() { lds_barrier(); };
+        // matrix phase M_m (registers only)
+        auto mphase = [&](int m) {
+            if (m < nsub) mma_qk(kf, s_cur);
+            if (m >= 1 && m - 1 < nsub) mma_pv(vf, p_cur);
+        };
+        // vector phase V_v; kbuf / vbuf: buffers of the tiles of sub-steps v+1 and v. The
+        // buffer offsets go through an opaque scalar so that the fragment addresses are one
+        // set of lane registers plus a uniform offset, not a register set per buffer.
+        auto opaque = [](int x) { asm volatile("" : "+s"(x)); return x; };
+        auto vphase = [&](int v, int kbuf, int vbuf, int cbuf) {
+            const LaneAddr la = lane_addr(lane);
+            if (v + 1 < nsub) load_k(v + 1, &sK[0][0] + opaque(kbuf * TILE_CHUNKS), la, kf);
+            if (v < nsub) {
+                load_v(v, &sV[0][0] + opaque(vbuf * TILE_CHUNKS), la, vf);
+                mask(v, s_cur);
+                Soft st;
+                softmax(s_cur, p_cur, st);
+                finish(st);
+            }
+            const int ct = v / 2 + 3;                 // tile whose copy half is issued here
+            if (ct < n_kt) copy_half(ct, v & 1, cbuf);
+        };
+        for (int a = 0; a < AHEAD; ++a)
+            if (a < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, a * tk, a * tv, lK[a], lV[a], wave);
+        load_q();
+        wait_vmcnt_barrier<0>();   // the Q loads are the newest: wait for everything once
+        {
+            const LaneAddr la = lane_addr(lane);
+            load_k(0, cKb[0], la, kf);
+        }
+        // step m = phases 2m and 2m+1; unrolled by 8 so that every buffer index is static.
+        // The two groups run separate copies of the loop (same barrier sequence).
+        auto step_barrier = [&](int m) {   // barrier that ends phase 2m
+            if ((m & 1) && (m + 1) / 2 < n_kt) wait_tile((m + 1) / 2);
+            else phase_barrier();
+        };
+        if (grp == 0) {
+            for (int m0 = 0; m0 <= nsub; m0 += 8) {
 #pragma unroll
-            for (int q = 0; q < 12; ++q) {
-                const int ph = pg + q;
-                if (ph >= nphase) break;
-                const int m = ph >> 1;
-                if ((q & 3) == 2) {                           // phase 4u+2: copy tile u+2
-                    const int t2 = (ph >> 2) + 2;
-                    const int b2 = ((q >> 2) + 2) % 3;
-                    if (t2 < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, t2 * tk, t2 * tv, lK[b2], lV[b2], wave);
+                for (int j = 0; j < 8; ++j) {
+                    const int m = m0 + j;
+                    if (m > nsub) break;
+                    mphase(m);                                                       // phase 2m
+                    step_barrier(m);
+                    vphase(m, ((j + 1) / 2) % 4, (j / 2) % 4, (j / 2 + 3) % 4);      // phase 2m+1
+                    phase_barrier();
                 }
-                if (grp == (q & 1)) {
-                    // M_m: P(m-1) V and S(m) = K Q^T
-                    const int kbuf = (q >> 2) % 3;            // tile m/2  (m/2 == ph/4)
-                    const int vbuf = ((q + 10) >> 2) % 3;     // tile (m-1)/2 == (ph-2)/4, mod 3
-                    const LaneAddr la = lane_addr(lane);
-                    if (m < nsub) qk(m, cKb[kbuf], sb, la);
-                    if (m >= 1 && m - 1 < nsub) pv(m - 1, cVb[vbuf], pb, la);
-                } else {
-                    const int v = m - 1 + (q & 1);
-                    if (v >= 0 && v < nsub) {
-                        mask(v, sb);
-                        Soft st;
-                        softmax(sb, pb, st);
-                        finish(st);
-                    }
+            }
+        } else {
+            for (int m0 = 0; m0 <= nsub; m0 += 8) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int m = m0 + j;
+                    if (m > nsub) break;
+                    // phase 2m: V_{m-1}, whose sub-step lies in tile m0/2 + (j + 7)/2 - 4
+                    if (m >= 1) vphase(m - 1, (j / 2) % 4, ((j + 7) / 2) % 4, ((j + 7) / 2 + 3) % 4);
+                    step_barrier(m);
+                    mphase(m);                                                       // phase 2m+1
+                    phase_barrier();
                 }
-                const bool period_end = (q & 3) == 3;         // next phase starts tile (ph+1)/4
-                const int tn = (ph + 1) >> 2;
-                phase_barrier(period_end && tn < n_kt, tn + 1 < n_kt);
             }
         }
     } else if constexpr (LOOP == 0) {
@@ -568,6 +628,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #pragma unroll
         for (int a = 0; a < AHEAD; ++a)
             if (a < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, a * tk, a * tv, lK[a], lV[a], wave);
+        load_q();
         for (int g = 0; NBUF * g < n_kt; ++g) {
 #pragma unroll
             for (int u = 0; u < NBUF; ++u) {
@@ -613,6 +674,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #pragma unroll
         for (int a = 0; a < AHEAD; ++a)
             if (a < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, a * tk, a * tv, lK[a], lV[a], wave);
+        load_q();
         for (int g = 0; NBUF * g < n_kt; ++g) {
 #pragma unroll
             for (int u = 0; u < NBUF; ++u) {
@@ -694,7 +756,7 @@ int mfma_loop() {
     static const int v = [] {
         const char* e = std::getenv("AULE_MFMA_LOOP");
         const int v = e ? std::atoi(e) : 1;
-        return (v >= 0 && v <= 3) ? v : 1;
+        return (v >= 0 && v <= 4) ? v : 1;
     }();
     return v;
 }
@@ -730,7 +792,8 @@ hipError_t launch_cfg(const AttnProblem& p, hipStream_t stream) {
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_gh(const AttnProblem& p, hipStream_t stream) {
     // loop form (AULE_MFMA_LOOP): 0 straight with 64-key tiles, 1 straight with 128-key
-    // tiles (default), 2 ping-pong with 64-key tiles, 3 pipelined sub-steps with 128-key tiles
+    // tiles (default), 2 ping-pong with 64-key tiles, 3 pipelined sub-steps with 128-key tiles,
+    // 4 straight with 64-key tiles in 4-wave workgroups (two workgroups per CU)
     const int gh = VARLEN ? 1 : heads_per_group(p.group);
     const int g = gh == 4 ? 2 : gh == 2 ? 1 : 0;
     switch (mfma_loop() * 3 + g) {
@@ -746,6 +809,9 @@ hipError_t launch_gh(const AttnProblem& p, hipStream_t stream) {
         case 9: return launch_cfg<T, D, 8, 1, 1, 128, 3, CAUSAL, VARLEN>(p, stream);
         case 10: return launch_cfg<T, D, 8, 1, 2, 128, 3, CAUSAL, VARLEN>(p, stream);
         case 11: return launch_cfg<T, D, 8, 1, 4, 128, 3, CAUSAL, VARLEN>(p, stream);
+        case 12: return launch_cfg<T, D, 4, 1, 1, 64, 0, CAUSAL, VARLEN>(p, stream);
+        case 13: return launch_cfg<T, D, 4, 1, 2, 64, 0, CAUSAL, VARLEN>(p, stream);
+        case 14: return launch_cfg<T, D, 4, 1, 4, 64, 0, CAUSAL, VARLEN>(p, stream);
     }
     return hipErrorInvalidValue;
 }
