@@ -203,9 +203,16 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_barrier" ::: "memory");
 }
 
-// TB: keys per K/V tile (64: three LDS buffers, copies requested two tiles ahead;
-// 128: two buffers, one tile ahead).
-template <typename T, int D, int WAVES, int NB, int GH, int TB, int LOOP, bool CAUSAL, bool VARLEN>
+// Parity of the LDS buffer that holds a work item's first K/V tile (persistent form), as a
+// type so that every buffer index stays a compile-time constant.
+template <int P> struct Parity { static constexpr int value = P; };
+
+// TB: keys per K/V tile. Eight-wave workgroups with 64-key tiles use three LDS buffers
+// (copies requested two tiles ahead); every other shape uses two (one tile ahead).
+// PERSIST (dense problems, two buffers): the grid holds one workgroup per CU and each walks
+// several work items, issuing the next item's first K/V tile copy and its Q loads while it
+// finishes the current item, so that their latency and the workgroup launch gap are hidden.
+template <typename T, int D, int WAVES, int NB, int GH, int TB, bool PERSIST, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -218,13 +225,12 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     constexpr int DB = D / 32;                   // 32-row d-blocks of O^T
     constexpr int kBN = TB;                      // keys per K/V tile
     constexpr int SPT = TB / 32;                 // 32-key sub-steps per tile
-    // LDS tile buffers: 4 for the ping-pong; 3 for 64-key tiles in 8-wave workgroups; else 2
-    // (4-wave workgroups keep two workgroups per CU within the LDS)
-    constexpr int NBUF = LOOP == 2 ? 4 : (TB == 64 && WAVES == 8 ? 3 : 2);
+    constexpr int NBUF = (TB == 64 && WAVES == 8) ? 3 : 2;   // LDS tile buffers
     constexpr int AHEAD = NBUF - 1;              // tiles requested ahead
     constexpr int DMA_PARTS = AULE_DMA_PARTS < SPT ? AULE_DMA_PARTS : SPT;   // pieces of a tile copy
+    constexpr int NSTORE = NB * DB * 4;          // O store instructions per wave and work item
     static_assert(TB == 64 || TB == 128, "tile of 64 or 128 keys");
-    static_assert(LOOP != 2 || TB == 64, "the ping-pong loop uses 64-key tiles");
+    static_assert(!PERSIST || (NBUF == 2 && !VARLEN), "persistent form: two buffers, dense problems");
     constexpr int TILE_CHUNKS = kBN * KC;        // 16-byte chunks per K (or V) tile
     constexpr int NI = TILE_CHUNKS / kThreads;   // load instructions per wave per tile
     static_assert(NI >= 1 && TILE_CHUNKS % kThreads == 0, "tile must split evenly over the waves");
@@ -234,59 +240,18 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    // wave-uniform (an SGPR): everything derived from it (rows, heads, ping-pong group,
-    // mask and barrier conditions) stays scalar, so those branches are scalar branches
+    // wave-uniform (an SGPR): everything derived from it (rows, heads, mask and barrier
+    // conditions) stays scalar, so those branches are scalar branches
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5;
     const int ln = lane & 31;
-
-    // ---------------------------------------------------------------- tile lookup
-    int bidx, hq0, tile, Lq, Lk;
-    int64_t tok0 = 0;
-    if constexpr (VARLEN) {
-        TileSlot s = locate_varlen_tile(p.cu_seqlens, p.batch, p.total_tokens, BMW, blockIdx.x, CAUSAL);
-        if (!s.valid) return;
-        bidx = s.seq; tok0 = s.tok0; tile = s.tile; Lq = s.len_q; Lk = s.len_k;
-        hq0 = blockIdx.y * GH;
-    } else {
-        // groups = (batch, GH query heads sharing one kv head). Workgroup x runs on XCD
-        // x % 8; when the groups split evenly, each XCD gets whole groups so their K/V stay
-        // in that XCD's L2. Within an XCD (or the whole grid) the longest causal tiles go first.
-        const int ngroups = p.heads_q / GH;
-        const int NG = p.batch * ngroups;
-        const int x = blockIdx.x;
-        int t, g;
-        if (NG % 8 == 0) {
-            const int per = NG / 8, xcd = x & 7, l = x >> 3;
-            t = l / per;
-            g = xcd * per + (l - t * per);
-        } else {
-            t = x / NG;
-            g = x - t * NG;
-        }
-        tile = CAUSAL ? (n_qtiles - 1 - t) : t;
-        bidx = g / ngroups;
-        hq0 = (g - bidx * ngroups) * GH;
-        Lq = p.seqlen_q; Lk = p.seqlen_k;
-    }
-    const int hq = hq0 + (wave % GH);
-    const int hk = hq0 / p.group;
-    const int qr0 = tile * BMW + kRowsPerWave * (wave / GH);   // first row of this wave
     const int hd = p.head_dim;
 
-    const T* qb = static_cast<const T*>(p.q) + (VARLEN ? tok0 * p.q_rstride : bidx * p.q_bstride) + hq * p.q_hstride;
-    const T* kb = static_cast<const T*>(p.k) + (VARLEN ? tok0 * p.k_rstride : bidx * p.k_bstride) + hk * p.k_hstride;
-    const T* vb = static_cast<const T*>(p.v) + (VARLEN ? tok0 * p.v_rstride : bidx * p.v_bstride) + hk * p.v_hstride;
-    T* ob = static_cast<T*>(p.o) + (VARLEN ? tok0 * p.o_rstride : bidx * p.o_bstride) + hq * p.o_hstride;
-
     // ---------------------------------------------------------------- K/V copy set-up
-    // Buffer descriptors cover exactly the Lk valid rows of this (sequence, kv head).
-    const uint32_t k_rs = (uint32_t)(p.k_rstride * (int64_t)sizeof(T));   // row stride, bytes
+    const uint32_t k_rs = (uint32_t)(p.k_rstride * (int64_t)sizeof(T));   // row strides, bytes
     const uint32_t v_rs = (uint32_t)(p.v_rstride * (int64_t)sizeof(T));
-    const int k_valid = Lk > 0 ? (int)((int64_t)(Lk - 1) * k_rs + hd * sizeof(T)) : 0;
-    const int v_valid = Lk > 0 ? (int)((int64_t)(Lk - 1) * v_rs + hd * sizeof(T)) : 0;
-    const i32x4 rsrc_k = buffer_desc(kb, k_valid);
-    const i32x4 rsrc_v = buffer_desc(vb, v_valid);
+    const uint32_t o_rs = (uint32_t)(p.o_rstride * (int64_t)sizeof(T));
+    const uint32_t q_rs = (uint32_t)(p.q_rstride * (int64_t)sizeof(T));
     // Per-lane byte offsets (tile-relative) of the global chunk that lands in this lane's
     // LDS slot, for each of the NI load instructions of this wave.
     uint32_t koff[NI], voff[NI];
@@ -298,24 +263,111 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         koff[i] = kdc * 8 < hd ? row * k_rs + kdc * 16 : kOobOffset;
         voff[i] = vdc * 8 < hd ? row * v_rs + vdc * 16 : kOobOffset;
     }
+
+    // ---------------------------------------------------------------- work items
+    // A work item is one q-tile of BMW rows of GH query heads that share one kv head (dense),
+    // or of one head of one sequence (varlen).
+    struct Item {
+        int Lq, Lk, qr0, nsub, n_kt;   // lengths, first row of this wave, sub-steps, K/V tiles
+        const T* qb;                   // this wave's Q slice and O slice
+        T* ob;
+        i32x4 rk, rv;                  // K / V slice descriptors, exactly the Lk valid rows
+    };
+    const int ngroups = p.heads_q / GH;
+    const int NG = p.batch * ngroups;
+    auto make_item = [&](int x, Item& it) -> bool {
+        int bidx, hq0, tile, Lq, Lk;
+        int64_t tok0 = 0;
+        if constexpr (VARLEN) {
+            TileSlot s = locate_varlen_tile(p.cu_seqlens, p.batch, p.total_tokens, BMW, x, CAUSAL);
+            if (!s.valid) return false;
+            bidx = s.seq; tok0 = s.tok0; tile = s.tile; Lq = s.len_q; Lk = s.len_k;
+            hq0 = blockIdx.y * GH;
+        } else {
+            // groups = (batch, GH query heads sharing one kv head). Item x runs on XCD x % 8
+            // (workgroup x does, and a persistent workgroup only takes items of its own XCD);
+            // when the groups split evenly, each XCD gets whole groups so that their K/V stay
+            // in that XCD's L2. Within an XCD (or the whole grid) the longest causal tiles
+            // come first.
+            if (x >= n_qtiles * NG) return false;
+            int t, g;
+            if (NG % 8 == 0) {
+                const int per = NG / 8, xcd = x & 7, l = x >> 3;
+                t = l / per;
+                g = xcd * per + (l - t * per);
+            } else {
+                t = x / NG;
+                g = x - t * NG;
+            }
+            tile = CAUSAL ? (n_qtiles - 1 - t) : t;
+            bidx = g / ngroups;
+            hq0 = (g - bidx * ngroups) * GH;
+            Lq = p.seqlen_q; Lk = p.seqlen_k;
+        }
+        const int hq = hq0 + (wave % GH);
+        const int hk = hq0 / p.group;
+        it.Lq = Lq;
+        it.Lk = Lk;
+        it.qr0 = tile * BMW + kRowsPerWave * (wave / GH);
+        it.qb = static_cast<const T*>(p.q) + (VARLEN ? tok0 * p.q_rstride : bidx * p.q_bstride) + hq * p.q_hstride;
+        it.ob = static_cast<T*>(p.o) + (VARLEN ? tok0 * p.o_rstride : bidx * p.o_bstride) + hq * p.o_hstride;
+        const T* kb = static_cast<const T*>(p.k) + (VARLEN ? tok0 * p.k_rstride : bidx * p.k_bstride) + hk * p.k_hstride;
+        const T* vb = static_cast<const T*>(p.v) + (VARLEN ? tok0 * p.v_rstride : bidx * p.v_bstride) + hk * p.v_hstride;
+        const int k_valid = Lk > 0 ? (int)((int64_t)(Lk - 1) * k_rs + hd * sizeof(T)) : 0;
+        const int v_valid = Lk > 0 ? (int)((int64_t)(Lk - 1) * v_rs + hd * sizeof(T)) : 0;
+        it.rk = buffer_desc(kb, k_valid);
+        it.rv = buffer_desc(vb, v_valid);
+        // The key range is walked in 32-key sub-steps, SPT per K/V tile. All waves of the
+        // workgroup walk the same sub-steps (a wave whose own rows end earlier gets fully
+        // masked sub-steps at the end, which add exact zeros).
+        const int wg_rows_end = min(tile * BMW + BMW, Lq);
+        const int keys_needed = CAUSAL ? wg_rows_end : Lk;
+        it.nsub = (keys_needed + 31) / 32;
+        it.n_kt = (it.nsub + SPT - 1) / SPT;
+        return true;
+    };
+    // Persistent form: the r-th item of this workgroup. Items of one XCD are dealt to its
+    // workgroups in snake order (forward in even rounds, backward in odd ones), which with
+    // the longest-first order balances the causal work across them.
+    auto item_x = [&](int r) -> int {
+        const int G = gridDim.x;
+        if (NG % 8 == 0 && G % 8 == 0) {
+            const int gx = G >> 3, w = blockIdx.x >> 3;
+            const int l = r * gx + ((r & 1) ? gx - 1 - w : w);
+            return l * 8 + (blockIdx.x & 7);
+        }
+        const int b = blockIdx.x;
+        return r * G + ((r & 1) ? G - 1 - b : b);
+    };
+
+    Item cur;
+    if (!make_item(PERSIST ? item_x(0) : (int)blockIdx.x, cur)) return;
+
     // ---------------------------------------------------------------- Q -> registers
-    // Issued after the first K/V tile copies (load_q is called from each loop's prologue) so
-    // that both latencies overlap; a negative scale flips Q's sign bits in a separate
-    // uniform branch, which is the only place that waits for the loads before the loop.
+    // Issued after the first K/V tile copy so that both latencies overlap; a negative scale
+    // flips Q's sign bits in a separate uniform branch (the only place that waits for the
+    // loads before the matrix products).
     const bool neg = p.scale_log2 < 0.f;
     const float c = fmaxf(fabsf(p.scale_log2), 1e-30f);
     u32x4 qf[NB][KS];
-    auto load_q = [&]() {
+    // Buffer loads whose descriptor covers the Lq valid rows: rows past the end read as
+    // zero, and one lane offset serves all k-steps (a scalar offset adds 32 bytes per step).
+    auto load_q = [&](const Item& it) {
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T*>(it.qb), (short)0, it.Lq > 0 ? (int)((int64_t)it.Lq * q_rs) : 0, (int)kBufferFlags);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-            const int row = qr0 + 32 * nb + ln;
+            const uint32_t off = (uint32_t)(it.qr0 + 32 * nb + ln) * q_rs + (uint32_t)h * 16u;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int col = (2 * ks + h) * 8;
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (row < Lq && col < hd) v = *reinterpret_cast<const u32x4*>(qb + (int64_t)row * p.q_rstride + col);
-                qf[nb][ks] = v;
-            }
+            for (int ks = 0; ks < KS; ++ks)
+                qf[nb][ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, ks * 32, 0));
+        }
+        if (hd < D) {   // columns past head_dim are zero (uniform branch)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    if ((2 * ks + h) * 8 >= hd) qf[nb][ks] = u32x4{0u, 0u, 0u, 0u};
         }
         if (neg) {
 #pragma unroll
@@ -325,24 +377,18 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         }
     };
 
-    // ---------------------------------------------------------------- sub-step ranges
-    // The key range is walked in 32-key sub-steps; sub-steps 2t and 2t+1 live in K/V tile t.
-    // All waves of the workgroup walk the same sub-steps (a wave whose own rows end earlier
-    // gets fully masked sub-steps at the end, which add exact zeros).
-    const int wg_rows_end = min(tile * BMW + BMW, Lq);
-    const int keys_needed = CAUSAL ? wg_rows_end : Lk;
-    const int nsub = (keys_needed + 31) / 32;
-    const int n_kt = (nsub + SPT - 1) / SPT;
-
     // ---------------------------------------------------------------- accumulators
     f32x16 o[DB][NB];
-#pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[db][nb] = f32x16{};
     float m_ref[NB], l_part[NB];
+    auto reset_acc = [&]() {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) { m_ref[nb] = -INFINITY; l_part[nb] = 0.f; }
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) o[db][nb] = f32x16{};
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) { m_ref[nb] = -INFINITY; l_part[nb] = 0.f; }
+    };
+    reset_acc();
 
     // Per-lane LDS address terms of the fragment reads. They are rebuilt from `lane` where
     // they are used; pinning `lane` with an empty asm per iteration stops the compiler from
@@ -379,14 +425,14 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     // -inf for keys past the end and (causal) keys after the query; a uniform branch
     auto mask = [&](int sub, f32x16 (&acc)[NB]) {
         const int k0 = 32 * sub;
-        if ((k0 + 32 > Lk) || (CAUSAL && k0 + 31 > qr0)) {
+        if ((k0 + 32 > cur.Lk) || (CAUSAL && k0 + 31 > cur.qr0)) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const int qi = qr0 + 32 * nb + ln;
+                const int qi = cur.qr0 + 32 * nb + ln;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + 16 * (r >> 3) + 8 * h + (r & 7);
-                    const bool masked = (key >= Lk) || (CAUSAL && key > qi);
+                    const bool masked = (key >= cur.Lk) || (CAUSAL && key > qi);
                     acc[nb][r] = masked ? -INFINITY : acc[nb][r];
                 }
             }
@@ -420,16 +466,6 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) o[db][nb] = Mfma<T>::mma(vf[cc][db], pf[cc][nb], o[db][nb]);
-    };
-    auto qk = [&](int sub, const u32x4* cK, f32x16 (&acc)[NB], const LaneAddr& la) {
-        u32x4 kf[KS];
-        load_k(sub, cK, la, kf);
-        mma_qk(kf, acc);
-    };
-    auto pv = [&](int sub, const u32x4* cV, const u32x4 (&pf)[2][NB], const LaneAddr& la) {
-        u32x4 vf[2][DB];
-        load_v(sub, cV, la, vf);
-        mma_pv(vf, pf);
     };
     // online softmax of one sub-step: P (packed 16-bit) relative to the possibly raised
     // reference max; the O / l rescale is applied by finish() after this sub-step's
@@ -509,12 +545,38 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         }
     };
 
+    // ---------------------------------------------------------------- epilogue
+    // O = O^T accumulators / l, rounded to T, through buffer stores whose descriptor covers
+    // exactly the Lq valid rows of this wave's slice: rows past the end and columns past
+    // head_dim (given an offset past the descriptor) are dropped by the hardware, so every
+    // wave issues exactly NSTORE store instructions per item, with no branch.
+    auto store_o = [&]() {
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            cur.ob, (short)0, cur.Lq > 0 ? (int)((int64_t)cur.Lq * o_rs) : 0, (int)kBufferFlags);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float l = l_part[nb] + __shfl_xor(l_part[nb], 32);
+            const float inv = 1.f / l;
+            const uint32_t rowoff = (uint32_t)(cur.qr0 + 32 * nb + ln) * o_rs;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int d0 = 32 * db + 8 * g + 4 * h;
+                    const u32x2 w = {Mfma<T>::pack2(o[db][nb][4 * g] * inv, o[db][nb][4 * g + 1] * inv),
+                                     Mfma<T>::pack2(o[db][nb][4 * g + 2] * inv, o[db][nb][4 * g + 3] * inv)};
+                    const uint32_t off = d0 < hd ? rowoff + (uint32_t)d0 * (uint32_t)sizeof(T) : kOobOffset;
+                    __builtin_amdgcn_raw_buffer_store_b64(w, ro, (int)off, 0, 0);
+                }
+        }
+    };
+
     // ---------------------------------------------------------------- main loop
-    // K/V tiles are triple buffered (tile t in buffer t % 3). Every buffer choice is a
+    // Tile t of an item sits in buffer (t + parity) % NBUF. Every buffer choice is a
     // compile-time one after unrolling, and every tile-copy completion is ordered by an
     // explicit s_waitcnt vmcnt + s_barrier (the copies are invisible to the compiler).
     const uint32_t tk = kBN * k_rs, tv = kBN * v_rs;   // bytes per K / V tile
-    auto lds_off = [](const u32x4* p) { return (uint32_t)(uintptr_t)(lds_void*)p; };
+    auto lds_off = [](const u32x4* q) { return (uint32_t)(uintptr_t)(lds_void*)q; };
     uint32_t lK[NBUF], lV[NBUF];
     const u32x4* cKb[NBUF];
     const u32x4* cVb[NBUF];
@@ -525,116 +587,25 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         cKb[b] = sK[b];
         cVb[b] = sV[b];
     }
-
     f32x16 s_cur[NB];
     u32x4 p_cur[2][NB];
 
-    if constexpr (LOOP == 2) {
-        // Ping-pong. The two waves of a SIMD (group 0: wave bit p.pp_shift clear, group 1:
-        // set) alternate between a matrix phase M_m = {S(m) = K Q^T, O += V^T P(m-1)} that
-        // reads only registers, and a vector phase V_v = {mask and softmax of sub-step v;
-        // LDS reads of the K fragments of v+1 and the V fragments of v; one half of a tile
-        // copy}. Phases end at a workgroup barrier; in phase 2m group 0 runs M_m while group
-        // 1 runs V_{m-1}, in phase 2m+1 group 0 runs V_m while group 1 runs M_m, so each
-        // SIMD always has one wave issuing matrix instructions and one doing vector work.
-        //
-        // Tiles of 64 keys (sub-steps 2T, 2T+1) rotate through four LDS buffers. Tile T is
-        // first read in phase 4T-1 (group 0 prefetching K of sub-step 2T) and last read in
-        // phase 4T+4; its copy is issued in V_{2T-6} (K half) and V_{2T-5} (V half), after
-        // tile T-4 (same buffer) was last read in phase 4T-12, and waited for at the
-        // barrier that ends phase 4T-2, when each wave has issued at most the copy of tile
-        // T+1 and the K half of tile T+2 after it.
-        static_assert(NBUF == 4 && AHEAD == 3 && SPT == 2, "ping-pong schedule assumes 64-key tiles in 4 buffers");
-        const int grp = (wave >> p.pp_shift) & 1;
-        u32x4 kf[KS];
-        u32x4 vf[2][DB];
-        auto copy_half = [&](int tile, int half, int buf) {
-            issue_tile_part<NI, 2>(half, rsrc_k, rsrc_v, koff, voff, tile * tk, tile * tv, lK[buf], lV[buf], wave);
-        };
-        auto wait_tile = [&](int tt) {   // at the barrier before phase 4tt-1
-            if (tt + 2 < n_kt) wait_vmcnt_barrier<3 * NI>();
-            else if (tt + 1 < n_kt) wait_vmcnt_barrier<2 * NI>();
-            else wait_vmcnt_barrier<0>();
-        };
-        auto phase_barrier = [&]() { lds_barrier(); };
-        // matrix phase M_m (registers only)
-        auto mphase = [&](int m) {
-            if (m < nsub) mma_qk(kf, s_cur);
-            if (m >= 1 && m - 1 < nsub) mma_pv(vf, p_cur);
-        };
-        // vector phase V_v; kbuf / vbuf: buffers of the tiles of sub-steps v+1 and v. The
-        // buffer offsets go through an opaque scalar so that the fragment addresses are one
-        // set of lane registers plus a uniform offset, not a register set per buffer.
-        auto opaque = [](int x) { asm volatile("" : "+s"(x)); return x; };
-        auto vphase = [&](int v, int kbuf, int vbuf, int cbuf) {
-            const LaneAddr la = lane_addr(lane);
-            if (v + 1 < nsub) load_k(v + 1, &sK[0][0] + opaque(kbuf * TILE_CHUNKS), la, kf);
-            if (v < nsub) {
-                load_v(v, &sV[0][0] + opaque(vbuf * TILE_CHUNKS), la, vf);
-                mask(v, s_cur);
-                Soft st;
-                softmax(s_cur, p_cur, st);
-                finish(st);
-            }
-            const int ct = v / 2 + 3;                 // tile whose copy half is issued here
-            if (ct < n_kt) copy_half(ct, v & 1, cbuf);
-        };
-        for (int a = 0; a < AHEAD; ++a)
-            if (a < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, a * tk, a * tv, lK[a], lV[a], wave);
-        load_q();
-        wait_vmcnt_barrier<0>();   // the Q loads are the newest: wait for everything once
-        {
-            const LaneAddr la = lane_addr(lane);
-            load_k(0, cKb[0], la, kf);
-        }
-        // step m = phases 2m and 2m+1; unrolled by 8 so that every buffer index is static.
-        // The two groups run separate copies of the loop (same barrier sequence).
-        auto step_barrier = [&](int m) {   // barrier that ends phase 2m
-            if ((m & 1) && (m + 1) / 2 < n_kt) wait_tile((m + 1) / 2);
-            else phase_barrier();
-        };
-        if (grp == 0) {
-            for (int m0 = 0; m0 <= nsub; m0 += 8) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int m = m0 + j;
-                    if (m > nsub) break;
-                    mphase(m);                                                       // phase 2m
-                    step_barrier(m);
-                    vphase(m, ((j + 1) / 2) % 4, (j / 2) % 4, (j / 2 + 3) % 4);      // phase 2m+1
-                    phase_barrier();
-                }
-            }
-        } else {
-            for (int m0 = 0; m0 <= nsub; m0 += 8) {
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int m = m0 + j;
-                    if (m > nsub) break;
-                    // phase 2m: V_{m-1}, whose sub-step lies in tile m0/2 + (j + 7)/2 - 4
-                    if (m >= 1) vphase(m - 1, (j / 2) % 4, ((j + 7) / 2) % 4, ((j + 7) / 2 + 3) % 4);
-                    step_barrier(m);
-                    mphase(m);                                                       // phase 2m+1
-                    phase_barrier();
-                }
-            }
-        }
-    } else if constexpr (LOOP == 0) {
-        // Straight loop: per 32-key sub-step S = K Q^T, mask, softmax, P V. Tile t sits in
-        // buffer t % NBUF. At the barrier before tile t each wave waits only for its copy
-        // of tile t (newer copies may stay in flight), then starts the copy of tile
-        // t + AHEAD into the buffer of tile t-1, which every wave finished before this
-        // barrier.
-#pragma unroll
-        for (int a = 0; a < AHEAD; ++a)
-            if (a < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, a * tk, a * tv, lK[a], lV[a], wave);
-        load_q();
-        for (int g = 0; NBUF * g < n_kt; ++g) {
+    // One item's tiles. `first`: no O stores of an earlier item are in flight; `more`: the
+    // next item (persistent form) exists and its first tile copy is issued after the barrier
+    // of this item's last tile (its Q loads follow the item, before the O stores).
+    auto run_item = [&](auto parity, bool first, bool more, const Item& nxt) {
+        constexpr int P = decltype(parity)::value;
+        for (int g = 0; NBUF * g < cur.n_kt; ++g) {
 #pragma unroll
             for (int u = 0; u < NBUF; ++u) {
                 const int t = NBUF * g + u;
-                if (t >= n_kt) break;
-                if (AHEAD == 2 && t + 1 < n_kt) wait_vmcnt_barrier<2 * NI>();   // tile t+1 may stay in flight
+                if (t >= cur.n_kt) break;
+                const int b = (u + P) % NBUF;
+                const int bn = (u + P + AHEAD) % NBUF;          // buffer of tile t + AHEAD
+                // at tile 0 of a later item the previous item's NSTORE stores are the newest
+                // memory operations and may stay in flight
+                if (PERSIST && t == 0 && !first) wait_vmcnt_barrier<NSTORE>();
+                else if (AHEAD == 2 && t + 1 < cur.n_kt) wait_vmcnt_barrier<2 * NI>();   // tile t+1 may stay in flight
                 else wait_vmcnt_barrier<0>();
                 // Fragment reads run one step ahead of their use: after the S^T products of
                 // sub-step i are issued, the V fragments of i and the K fragments of i+1 are
@@ -642,21 +613,23 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                 // t + AHEAD is issued in DMA_PARTS pieces, one after each of the first
                 // DMA_PARTS sub-steps' S^T products (every sub-step of a tile that is not the
                 // last one runs, so all pieces are issued before the next barrier).
+                const bool copy_next = t + AHEAD < cur.n_kt;
+                if (PERSIST && more && t + 1 == cur.n_kt)
+                    issue_tile<NI>(nxt.rk, nxt.rv, koff, voff, 0, 0, lK[bn], lV[bn], wave);
                 const LaneAddr la = lane_addr(lane);
                 u32x4 kf[KS];
                 u32x4 vf[2][DB];
-                load_k(SPT * t, cKb[u], la, kf);
-                const bool copy_next = t + AHEAD < n_kt;
+                load_k(SPT * t, cKb[b], la, kf);
 #pragma unroll
-                for (int h = 0; h < SPT; ++h) {
-                    const int i = SPT * t + h;
-                    if (i >= nsub) break;
+                for (int hh = 0; hh < SPT; ++hh) {
+                    const int i = SPT * t + hh;
+                    if (i >= cur.nsub) break;
                     mma_qk(kf, s_cur);
-                    if (h < DMA_PARTS && copy_next)
-                        issue_tile_part<NI, DMA_PARTS>(h, rsrc_k, rsrc_v, koff, voff, (t + AHEAD) * tk, (t + AHEAD) * tv,
-                                                       lK[(u + AHEAD) % NBUF], lV[(u + AHEAD) % NBUF], wave);
-                    load_v(i, cVb[u], la, vf);
-                    if (h + 1 < SPT) load_k(i + 1, cKb[u], la, kf);
+                    if (hh < DMA_PARTS && copy_next)
+                        issue_tile_part<NI, DMA_PARTS>(hh, cur.rk, cur.rv, koff, voff, (t + AHEAD) * tk, (t + AHEAD) * tv,
+                                                       lK[bn], lV[bn], wave);
+                    load_v(i, cVb[b], la, vf);
+                    if (hh + 1 < SPT) load_k(i + 1, cKb[b], la, kf);
                     mask(i, s_cur);
                     Soft st;
                     softmax(s_cur, p_cur, st);
@@ -665,153 +638,103 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                 }
             }
         }
-    } else if constexpr (LOOP == 3) {
-        // Straight tiles with the sub-steps pipelined inside each wave: the S^T products of
-        // sub-step i+1 are issued interleaved with the softmax of sub-step i (one matrix
-        // instruction, then a slice of vector work), so a wave keeps the matrix unit fed
-        // while it exponentiates. V fragments are read after the K fragments are dead, to
-        // stay within the register budget of two waves per SIMD.
-#pragma unroll
-        for (int a = 0; a < AHEAD; ++a)
-            if (a < n_kt) issue_tile<NI>(rsrc_k, rsrc_v, koff, voff, a * tk, a * tv, lK[a], lV[a], wave);
-        load_q();
-        for (int g = 0; NBUF * g < n_kt; ++g) {
-#pragma unroll
-            for (int u = 0; u < NBUF; ++u) {
-                const int t = NBUF * g + u;
-                if (t >= n_kt) break;
-                if (AHEAD == 2 && t + 1 < n_kt) wait_vmcnt_barrier<2 * NI>();
-                else wait_vmcnt_barrier<0>();
-                const bool copy_next = t + AHEAD < n_kt;
-                const LaneAddr la = lane_addr(lane);
-                const int i0 = SPT * t;
-                {
-                    u32x4 kf[KS];
-                    load_k(i0, cKb[u], la, kf);
-                    mma_qk(kf, s_cur);
-                }
-#pragma unroll
-                for (int h = 0; h < SPT; ++h) {
-                    const int i = i0 + h;
-                    if (i >= nsub) break;
-                    if (h < DMA_PARTS && copy_next)
-                        issue_tile_part<NI, DMA_PARTS>(h, rsrc_k, rsrc_v, koff, voff, (t + AHEAD) * tk, (t + AHEAD) * tv,
-                                                       lK[(u + AHEAD) % NBUF], lV[(u + AHEAD) % NBUF], wave);
-                    mask(i, s_cur);
-                    const bool more = (h + 1 < SPT) && (i + 1 < nsub);
-                    f32x16 s_nxt[NB];
-                    Soft st;
-                    if (more) {
-                        u32x4 kf[KS];
-                        load_k(i + 1, cKb[u], la, kf);
-                        mma_qk(kf, s_nxt);
-                        softmax(s_cur, p_cur, st);
-                    } else {
-                        softmax(s_cur, p_cur, st);
-                    }
-                    finish(st);
-                    {
-                        u32x4 vf[2][DB];
-                        load_v(i, cVb[u], la, vf);
-                        mma_pv(vf, p_cur);
-                    }
-                    if (more) {
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) s_cur[nb] = s_nxt[nb];
-                    }
-                }
-            }
+    };
+
+    if constexpr (PERSIST) {
+        issue_tile<NI>(cur.rk, cur.rv, koff, voff, 0, 0, lK[0], lV[0], wave);
+        load_q(cur);
+        int par = 0;   // buffer of the current item's first tile
+        for (int r = 0;; ++r) {
+            Item nxt;
+            const bool more = make_item(item_x(r + 1), nxt);
+            if (par == 0) run_item(Parity<0>{}, r == 0, more, nxt);
+            else run_item(Parity<1>{}, r == 0, more, nxt);
+            if (more) load_q(nxt);   // Q is dead after this item's last S^T products
+            store_o();
+            if (!more) break;
+            par = (par + cur.n_kt) & 1;
+            cur = nxt;
+            reset_acc();
         }
     } else {
-        static_assert(LOOP == 0 || LOOP == 2 || LOOP == 3, "loop form");
-    }
-
-    // ---------------------------------------------------------------- epilogue
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-        const float l = l_part[nb] + __shfl_xor(l_part[nb], 32);
-        const float inv = 1.f / l;
-        const int row = qr0 + 32 * nb + ln;
-        if (row < Lq) {
-            T* orow = ob + (int64_t)row * p.o_rstride;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int d0 = 32 * db + 8 * g + 4 * h;
-                    if (d0 < hd) {
-                        u32x2 w = {Mfma<T>::pack2(o[db][nb][4 * g] * inv, o[db][nb][4 * g + 1] * inv),
-                                   Mfma<T>::pack2(o[db][nb][4 * g + 2] * inv, o[db][nb][4 * g + 3] * inv)};
-                        *reinterpret_cast<u32x2*>(orow + d0) = w;
-                    }
-                }
-        }
+        for (int a = 0; a < AHEAD; ++a)
+            if (a < cur.n_kt) issue_tile<NI>(cur.rk, cur.rv, koff, voff, a * tk, a * tv, lK[a], lV[a], wave);
+        load_q(cur);
+        run_item(Parity<0>{}, true, false, cur);
+        store_o();
     }
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
 int heads_per_group(int group) { return (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1; }
 
+// Kernel form (AULE_MFMA_LOOP): 0 straight with 64-key tiles (three buffers), 1 straight
+// with 128-key tiles (two buffers), 4 straight with 64-key tiles in 4-wave workgroups (two
+// workgroups per CU), 5 persistent over 128-key tiles (default; varlen problems use form 1).
 int mfma_loop() {
     static const int v = [] {
         const char* e = std::getenv("AULE_MFMA_LOOP");
-        const int v = e ? std::atoi(e) : 1;
-        return (v >= 0 && v <= 4) ? v : 1;
-    }();
-    return v;
-}
-// which wave-index bit splits the ping-pong groups (waves w and w+4 share a SIMD: bit 2)
-int pp_shift() {
-    static const int v = [] {
-        const char* e = std::getenv("AULE_PP_SHIFT");
-        const int v = e ? std::atoi(e) : 2;
-        return (v >= 0 && v <= 2) ? v : 2;
+        const int v = e ? std::atoi(e) : 5;
+        return (v == 0 || v == 1 || v == 4 || v == 5) ? v : 5;
     }();
     return v;
 }
 
-template <typename T, int D, int WAVES, int NB, int GH, int TB, int LOOP, bool CAUSAL, bool VARLEN>
+// workgroups that fit on the device at once for the persistent form (one per CU)
+int resident_workgroups() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    return n;
+}
+
+template <typename T, int D, int WAVES, int NB, int GH, int TB, bool PERSIST, bool CAUSAL, bool VARLEN>
 hipError_t launch_cfg(const AttnProblem& p, hipStream_t stream) {
     constexpr int BMW = 32 * NB * (WAVES / GH);
     dim3 block(WAVES * 64);
-    AttnProblem pp = p;
-    pp.pp_shift = pp_shift();
     if constexpr (VARLEN) {
         dim3 grid(varlen_grid_tiles(p.total_tokens, p.batch, BMW), p.heads_q / GH, 1);
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, TB, LOOP, CAUSAL, true>), grid, block, 0, stream, pp, 0);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, TB, PERSIST, CAUSAL, true>), grid, block, 0, stream, p, 0);
     } else {
         const int n_qtiles = (p.seqlen_q + BMW - 1) / BMW;
-        const int64_t nblocks = (int64_t)n_qtiles * p.batch * (p.heads_q / GH);
-        if (nblocks > INT32_MAX) return hipErrorInvalidConfiguration;
+        const int64_t nitems = (int64_t)n_qtiles * p.batch * (p.heads_q / GH);
+        if (nitems > INT32_MAX) return hipErrorInvalidConfiguration;
+        int64_t nblocks = nitems;
+        if constexpr (PERSIST) {
+            static const int resident = resident_workgroups();
+            const int64_t g = resident >= 8 ? resident / 8 * 8 : resident;
+            if (nblocks > g) nblocks = g;
+        }
         dim3 grid((unsigned)nblocks);
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, TB, LOOP, CAUSAL, false>), grid, block, 0, stream, pp, n_qtiles);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, TB, PERSIST, CAUSAL, false>), grid, block, 0, stream, p, n_qtiles);
     }
     return hipGetLastError();
 }
 
 template <typename T, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_gh(const AttnProblem& p, hipStream_t stream) {
-    // loop form (AULE_MFMA_LOOP): 0 straight with 64-key tiles, 1 straight with 128-key
-    // tiles (default), 2 ping-pong with 64-key tiles, 3 pipelined sub-steps with 128-key tiles,
-    // 4 straight with 64-key tiles in 4-wave workgroups (two workgroups per CU)
     const int gh = VARLEN ? 1 : heads_per_group(p.group);
     const int g = gh == 4 ? 2 : gh == 2 ? 1 : 0;
-    switch (mfma_loop() * 3 + g) {
-        case 0: return launch_cfg<T, D, 8, 1, 1, 64, 0, CAUSAL, VARLEN>(p, stream);
-        case 1: return launch_cfg<T, D, 8, 1, 2, 64, 0, CAUSAL, VARLEN>(p, stream);
-        case 2: return launch_cfg<T, D, 8, 1, 4, 64, 0, CAUSAL, VARLEN>(p, stream);
-        case 3: return launch_cfg<T, D, 8, 1, 1, 128, 0, CAUSAL, VARLEN>(p, stream);
-        case 4: return launch_cfg<T, D, 8, 1, 2, 128, 0, CAUSAL, VARLEN>(p, stream);
-        case 5: return launch_cfg<T, D, 8, 1, 4, 128, 0, CAUSAL, VARLEN>(p, stream);
-        case 6: return launch_cfg<T, D, 8, 1, 1, 64, 2, CAUSAL, VARLEN>(p, stream);
-        case 7: return launch_cfg<T, D, 8, 1, 2, 64, 2, CAUSAL, VARLEN>(p, stream);
-        case 8: return launch_cfg<T, D, 8, 1, 4, 64, 2, CAUSAL, VARLEN>(p, stream);
-        case 9: return launch_cfg<T, D, 8, 1, 1, 128, 3, CAUSAL, VARLEN>(p, stream);
-        case 10: return launch_cfg<T, D, 8, 1, 2, 128, 3, CAUSAL, VARLEN>(p, stream);
-        case 11: return launch_cfg<T, D, 8, 1, 4, 128, 3, CAUSAL, VARLEN>(p, stream);
-        case 12: return launch_cfg<T, D, 4, 1, 1, 64, 0, CAUSAL, VARLEN>(p, stream);
-        case 13: return launch_cfg<T, D, 4, 1, 2, 64, 0, CAUSAL, VARLEN>(p, stream);
-        case 14: return launch_cfg<T, D, 4, 1, 4, 64, 0, CAUSAL, VARLEN>(p, stream);
+    int form = mfma_loop();
+    if (VARLEN && form == 5) form = 1;
+    switch (form * 3 + g) {
+        case 0: return launch_cfg<T, D, 8, 1, 1, 64, false, CAUSAL, VARLEN>(p, stream);
+        case 1: return launch_cfg<T, D, 8, 1, 2, 64, false, CAUSAL, VARLEN>(p, stream);
+        case 2: return launch_cfg<T, D, 8, 1, 4, 64, false, CAUSAL, VARLEN>(p, stream);
+        case 3: return launch_cfg<T, D, 8, 1, 1, 128, false, CAUSAL, VARLEN>(p, stream);
+        case 4: return launch_cfg<T, D, 8, 1, 2, 128, false, CAUSAL, VARLEN>(p, stream);
+        case 5: return launch_cfg<T, D, 8, 1, 4, 128, false, CAUSAL, VARLEN>(p, stream);
+        case 12: return launch_cfg<T, D, 4, 1, 1, 64, false, CAUSAL, VARLEN>(p, stream);
+        case 13: return launch_cfg<T, D, 4, 1, 2, 64, false, CAUSAL, VARLEN>(p, stream);
+        case 14: return launch_cfg<T, D, 4, 1, 4, 64, false, CAUSAL, VARLEN>(p, stream);
+    }
+    if constexpr (!VARLEN) {
+        switch (g) {
+            case 0: return launch_cfg<T, D, 8, 1, 1, 128, true, CAUSAL, false>(p, stream);
+            case 1: return launch_cfg<T, D, 8, 1, 2, 128, true, CAUSAL, false>(p, stream);
+            case 2: return launch_cfg<T, D, 8, 1, 4, 128, true, CAUSAL, false>(p, stream);
+        }
     }
     return hipErrorInvalidValue;
 }
@@ -835,10 +758,13 @@ bool mfma_supports(const AttnProblem& p, Dtype dt) {
     if (!(dt == Dtype::F16 || dt == Dtype::BF16) || p.head_dim > 128 || p.head_dim % 8 != 0) return false;
     // K/V copies address one (sequence, kv head) slice with 32-bit buffer offsets; keep the
     // slice plus one tile of offset headroom below 2^30 bytes.
-    const int64_t rows = p.cu_seqlens ? p.total_tokens : p.seqlen_k;
-    const int64_t stride = p.k_rstride > p.v_rstride ? p.k_rstride : p.v_rstride;
-    const int64_t bytes = (rows + 128) * stride * 2;
-    return bytes < (int64_t(1) << 30);
+    // The same holds for the Q loads and O stores, which address one slice of Q / O.
+    const int64_t rows_k = p.cu_seqlens ? p.total_tokens : p.seqlen_k;
+    const int64_t rows_q = p.cu_seqlens ? p.total_tokens : p.seqlen_q;
+    const int64_t stride_k = p.k_rstride > p.v_rstride ? p.k_rstride : p.v_rstride;
+    const int64_t stride_q = p.q_rstride > p.o_rstride ? p.q_rstride : p.o_rstride;
+    const int64_t limit = int64_t(1) << 30;
+    return (rows_k + 256) * stride_k * 2 < limit && (rows_q + 256) * stride_q * 2 < limit;
 }
 
 hipError_t launch_attn_fwd_mfma(const AttnProblem& p, Dtype dt, hipStream_t stream) {

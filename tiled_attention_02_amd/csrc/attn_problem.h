@@ -37,7 +37,6 @@ struct AttnProblem {
     const int32_t* cu_seqlens;  // varlen only, else nullptr
     int32_t total_tokens;       // varlen only
     int32_t max_seqlen;         // varlen hint
-    int32_t pp_shift;           // MFMA kernel: wave-index bit that splits ping-pong groups
 };
 
 // Launchers. Each returns hipSuccess or the launch error; none synchronises.
