@@ -35,6 +35,11 @@ Sources for each step:
 Readings where the pages are silent:
   * causal masking is top-left (key j is visible to query i iff j <= i) and needs
     seqlen_q == seqlen_k; the pages only show equal lengths;
+  * decoding against a KV cache (FlashAttention-T commentary, FAQ 4, inference bullet:
+    the KV cache is processed in blocks) is attention of Nq <= Nk new queries against all
+    Nk cached keys; under causal masking the new queries are the last Nq positions of the
+    sequence (bottom-right alignment: query i sees keys j <= i + Nk - Nq), so decoding them
+    reproduces the last Nq rows of causal attention over the whole sequence;
   * the scale is applied to the float64 dot product as the exact float32 value the
     library receives;
   * inputs are the values already rounded to the storage dtype (the generators do that);
@@ -184,4 +189,35 @@ def attention_ref_varlen_rows(qkv, cu_seqlens, tokens, *, causal: bool,
         q, k, v = _seq_as_dense(qkv, a, e)
         res = attention_ref_rows(q, k, v, local, causal=causal, scale=scale)[0]
         out[sel] = res.transpose(1, 0, 2)
+    return out
+
+
+def _decode_masked(n_queries: int, n_keys: int) -> np.ndarray:
+    """Boolean [n_queries, n_keys]: True where key j lies after query i, the queries being
+    the last n_queries positions of an n_keys-long sequence."""
+    shift = n_keys - n_queries
+    return np.arange(n_keys)[None, :] > (np.arange(n_queries) + shift)[:, None]
+
+
+def attention_ref_decode(q, k, v, *, causal: bool, scale: float) -> np.ndarray:
+    """Attention of Nq new queries against an Nk-long key/value cache, q: [B,Hq,Nq,d],
+    k, v: [B,Hkv,Nk,d], Nq <= Nk when causal, with bottom-right causal alignment (query i
+    is sequence position Nk - Nq + i). Without masking it is attention_ref. Returns float64
+    [B,Hq,Nq,d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Hkv, Nq, Nk, d = _check_dense(q, k, v, False)
+    if causal and Nq > Nk:
+        raise ValueError("causal decoding needs seqlen_q <= seqlen_k")
+    G = Hq // Hkv
+    sc = _scale64(scale)
+    out = np.empty((B, Hq, Nq, d), dtype=np.float64)
+    if causal:
+        masked = _decode_masked(Nq, Nk)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = _kv_head(hq, G)
+            S = sc * (q[b, hq] @ k[b, hk].T)
+            if causal:
+                S[masked] = -np.inf
+            out[b, hq] = _softmax_rows_times_v(S, v[b, hk])
     return out

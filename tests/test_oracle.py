@@ -297,8 +297,9 @@ def test_dense_validation():
 
 # ---------------------------------------------------------------- brute force
 
-def brute_force(q, k, v, causal, scale):
-    """Pure-Python loops with math.exp: no numpy arithmetic at all."""
+def brute_force(q, k, v, causal, scale, shift=0):
+    """Pure-Python loops with math.exp: no numpy arithmetic at all. With ``shift``, query i
+    sees keys j <= i + shift under causal masking."""
     B, Hq, Nq, d = q.shape
     Hkv, Nk = k.shape[1], k.shape[2]
     G = Hq // Hkv
@@ -310,7 +311,7 @@ def brute_force(q, k, v, causal, scale):
             for i in range(Nq):
                 scores = []
                 for j in range(Nk):
-                    if causal and j > i:
+                    if causal and j > i + shift:
                         continue
                     dot = 0.0
                     for c in range(d):
@@ -432,6 +433,66 @@ def test_config1_full_oracle_runs():
     assert o.shape == q.shape and np.all(np.isfinite(o))
 
 
+# ---------------------------------------------------------------- decoding against a KV cache
+
+@pytest.mark.parametrize("Nq", [1, 2, 5, 16])
+def test_decode_tail_of_full_causal(Nq):
+    """Decoding the last Nq positions against the whole cache reproduces the last Nq rows
+    of causal attention over the full sequence."""
+    rng = np.random.default_rng(300 + Nq)
+    Nk, d, Hkv, G = 16, 8, 2, 2
+    q_full = rng.standard_normal((2, Hkv * G, Nk, d))
+    k = rng.standard_normal((2, Hkv, Nk, d))
+    v = rng.standard_normal((2, Hkv, Nk, d))
+    full = oracle.attention_ref(q_full, k, v, causal=True, scale=0.4)
+    dec = oracle.attention_ref_decode(q_full[:, :, Nk - Nq:], k, v, causal=True, scale=0.4)
+    np.testing.assert_allclose(dec, full[:, :, Nk - Nq:], rtol=0, atol=1e-12)
+
+
+def test_decode_single_query_sees_whole_cache():
+    rng = np.random.default_rng(311)
+    q = rng.standard_normal((1, 4, 1, 16))
+    k = rng.standard_normal((1, 2, 37, 16))
+    v = rng.standard_normal((1, 2, 37, 16))
+    a = oracle.attention_ref_decode(q, k, v, causal=True, scale=0.25)
+    b = oracle.attention_ref(q, k, v, causal=False, scale=0.25)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_decode_noncausal_is_plain_attention():
+    rng = np.random.default_rng(312)
+    q = rng.standard_normal((2, 2, 3, 8))
+    k = rng.standard_normal((2, 1, 9, 8))
+    v = rng.standard_normal((2, 1, 9, 8))
+    np.testing.assert_allclose(oracle.attention_ref_decode(q, k, v, causal=False, scale=1.3),
+                               oracle.attention_ref(q, k, v, causal=False, scale=1.3),
+                               rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_brute_force_tiny(seed):
+    rng = np.random.default_rng(320 + seed)
+    Hkv, G = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    Nk = int(rng.integers(1, 9))
+    Nq = int(rng.integers(1, Nk + 1))
+    d = int(rng.integers(1, 7))
+    scale = float(rng.uniform(-2, 2))
+    q = rng.standard_normal((1, Hkv * G, Nq, d))
+    k = rng.standard_normal((1, Hkv, Nk, d))
+    v = rng.standard_normal((1, Hkv, Nk, d))
+    ref = brute_force(q, k, v, True, scale, shift=Nk - Nq)
+    got = oracle.attention_ref_decode(q, k, v, causal=True, scale=scale)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_decode_validation():
+    q = np.zeros((1, 1, 5, 4))
+    k = np.zeros((1, 1, 4, 4))
+    with pytest.raises(ValueError):
+        oracle.attention_ref_decode(q, k, k, causal=True, scale=1.0)
+    oracle.attention_ref_decode(q, k, k, causal=False, scale=1.0)   # non-causal: any Nq
+
+
 # ---------------------------------------------------------------- mutation checks
 
 def _pins_pass():
@@ -447,6 +508,8 @@ def _pins_pass():
         lambda: test_dominant_key("full", False),
         lambda: test_varlen_golden_cu_seqlens_example(),
         lambda: test_single_key_returns_v("full", 0.125),
+        lambda: test_decode_tail_of_full_causal(5),
+        lambda: test_decode_brute_force_tiny(0),
     ]
     for c in checks:
         try:
@@ -490,6 +553,10 @@ MUTANTS = {
     "softmax_sign_flipped": ("_softmax_rows_times_v", _mut_softmax_sign),
     "scale_inverted": ("_scale64", lambda s: 1.0 / float(np.float32(s)) if s else 0.0),
     "scale_dropped": ("_scale64", lambda s: 1.0),
+    "decode_mask_top_left": ("_decode_masked",
+                             lambda nq, nk: np.arange(nk)[None, :] > np.arange(nq)[:, None]),
+    "decode_mask_includes_next_key": ("_decode_masked",
+                                      lambda nq, nk: np.arange(nk)[None, :] > (np.arange(nq) + nk - nq + 1)[:, None]),
 }
 
 
