@@ -75,9 +75,9 @@ def parse():
 
 
 def device_inputs(cfg, torch):
-    from workloads import DenseConfig
+    from workloads import DecodeConfig, DenseConfig
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
-    if isinstance(cfg, DenseConfig):
+    if isinstance(cfg, (DenseConfig, DecodeConfig)):
         q, k, v = cfg.inputs()
         t = lambda x: torch.from_numpy(x).to(device="cuda", dtype=tdt)
         return (t(q), t(k), t(v)), (q, k, v)
@@ -88,7 +88,16 @@ def device_inputs(cfg, torch):
 
 def make_step(cfg, dev_inputs, torch):
     import tiled_attention_02_amd as aule
-    from workloads import DenseConfig
+    from workloads import DecodeConfig, DenseConfig
+    if isinstance(cfg, DecodeConfig):
+        q, k, v = dev_inputs
+        out = torch.empty_like(q)
+        B, Hq, Nq, d = q.shape
+        need = aule.aule_attn_splitkv_workspace_size(B, Hq, k.shape[1], Nq, k.shape[2], d,
+                                                     aule.dtype_code(q.dtype), 0)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)   # outside the timed region
+        return lambda: aule.flash_attention_decode(q, k, v, causal=cfg.causal,
+                                                   scale=cfg.softmax_scale, out=out, workspace=ws)
     if isinstance(cfg, DenseConfig):
         q, k, v = dev_inputs
         out = torch.empty_like(q)
@@ -125,8 +134,31 @@ def cpu_baseline(cfg, host_inputs, budget_s):
     fit in about budget_s seconds; scaled to TFLOP/s with the same FLOP count."""
     import numpy as np
     import oracle
-    from workloads import DenseConfig
+    from workloads import DecodeConfig, DenseConfig
     threads = len(os.sched_getaffinity(0))
+    if isinstance(cfg, DecodeConfig):
+        # whole (batch, query head) slices against their kv head's cache; scaled to GB/s of
+        # the workload's compulsory bytes like the GPU figure
+        q, k, v = host_inputs
+        G = cfg.heads_q // cfg.heads_kv
+        total = cfg.batch * cfg.heads_q
+        t0 = time.perf_counter()
+        done = 0
+        for b in range(cfg.batch):
+            for hq in range(cfg.heads_q):
+                hk = hq // G
+                oracle.attention_ref_decode(q[b:b + 1, hq:hq + 1], k[b:b + 1, hk:hk + 1],
+                                            v[b:b + 1, hk:hk + 1], causal=cfg.causal,
+                                            scale=cfg.softmax_scale)
+                done += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            if time.perf_counter() - t0 > budget_s:
+                break
+        dt = time.perf_counter() - t0
+        return {"value": cfg.bytes_compulsory() * done / total / dt / 1e9, "unit": "GB/s",
+                "cores": threads, "kind": "oracle",
+                "sample": f"{done} of {total} (batch, query head) slices, {dt:.1f} s"}
     if not isinstance(cfg, DenseConfig):
         qkv, cu = host_inputs
         t0 = time.perf_counter()
@@ -178,7 +210,8 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
-    from workloads import CONFIGS
+    from workloads import CONFIGS, DECODE_CONFIGS, DecodeConfig
+    ALL = {**CONFIGS, **DECODE_CONFIGS}
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
@@ -190,7 +223,7 @@ def main():
         print(json.dumps({"copy_bytes": n, "launches": max(1, args.steps)}), flush=True)
         return
 
-    cfg = CONFIGS[args.workload]
+    cfg = ALL[args.workload]
     dev_in, host_in = device_inputs(cfg, torch)
     step = make_step(cfg, dev_in, torch)
     wall_s, kern_s = time_steps(step, args.steps, args.warmup, torch)
@@ -220,16 +253,26 @@ def main():
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": cfg.bytes_compulsory()},
     }
+    if isinstance(cfg, DecodeConfig):
+        # reading the KV cache bounds this path: throughput against the HBM roofline
+        gbs = cfg.bytes_compulsory() / kern_s / 1e9
+        line["metric"] = "attention decode (split-KV) achieved HBM GB/s"
+        line["value"] = round(cfg.bytes_compulsory() / wall_s / 1e9, 1)
+        line["unit"] = "GB/s"
+        line["config"]["pct_of_peak"] = round(100 * line["value"] / HBM_PEAK_GBS, 2)
+        line["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)})
     if args.all:
-        for name, c in CONFIGS.items():
+        for name, c in ALL.items():
             if name == cfg.name:
                 continue
             di, _ = device_inputs(c, torch)
             w, kt = time_steps(make_step(c, di, torch), max(5, args.steps // 5), 3, torch)
             pk = MFMA_PEAK_TFLOPS[c.dtype]
+            gbs = c.bytes_compulsory() / kt / 1e9
             print(f"[bench] {name}: {kt * 1e3:.4f} ms/launch, {c.flops() / kt / 1e12:.1f} TFLOP/s "
                   f"({100 * c.flops() / kt / 1e12 / pk:.1f}% of {pk:.0f}), "
-                  f"{c.bytes_compulsory() / kt / 1e9:.0f} GB/s compulsory", file=sys.stderr)
+                  f"{gbs:.0f} GB/s compulsory ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)", file=sys.stderr)
             del di
             torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
@@ -238,7 +281,11 @@ def main():
 
 
 def describe(cfg):
-    from workloads import DenseConfig
+    from workloads import DecodeConfig, DenseConfig
+    if isinstance(cfg, DecodeConfig):
+        return (f"{cfg.dtype} decode {'causal' if cfg.causal else 'non-causal'} B={cfg.batch} "
+                f"Hq={cfg.heads_q} Hkv={cfg.heads_kv} Nq={cfg.seqlen_q} Nk={cfg.seqlen_k} "
+                f"d={cfg.head_dim} scale={cfg.softmax_scale:.6g}")
     if isinstance(cfg, DenseConfig):
         return (f"{cfg.dtype} {'causal' if cfg.causal else 'non-causal'} B={cfg.batch} Hq={cfg.heads_q} "
                 f"Hkv={cfg.heads_kv} N={cfg.seqlen} d={cfg.head_dim} scale={cfg.softmax_scale:.6g}")

@@ -26,6 +26,7 @@
 #ifndef AULE_ATTN_H
 #define AULE_ATTN_H
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h> /* hipStream_t */
 
@@ -101,6 +102,51 @@ aule_status_t aule_attn_fwd_varlen(const void* qkv, const int32_t* cu_seqlens, v
                                    int32_t max_seqlen, int32_t heads, int32_t head_dim,
                                    int32_t causal, float scale, aule_dtype_t dtype,
                                    hipStream_t stream);
+
+/*
+ * Attention of a few new queries against a key/value cache (decoding), split over the key
+ * range.
+ *
+ * Operation: the same attention as aule_attn_fwd (same layouts, GQA head mapping, dtype and
+ * scale rules) for seqlen_q new queries per sequence against seqlen_k cached keys, with the
+ * KV cache processed in blocks as the FlashAttention-T commentary (ai-stack.site, FAQ 4,
+ * inference bullet) describes for inference. Under `causal` the new queries are the last
+ * seqlen_q positions of the sequence: query i sees keys j <= i + seqlen_k - seqlen_q
+ * (bottom-right alignment; equal to aule_attn_fwd's mask when seqlen_q == seqlen_k).
+ *
+ * The key range is cut into splits, each reduced to a partial row max, row sum and
+ * unnormalised output in fp32 in `workspace`, then merged into o. The workspace is DEVICE
+ * memory owned by the caller, at least aule_attn_splitkv_workspace_size(...) bytes for the
+ * same arguments, 16-byte aligned, not overlapping any tensor; its contents on entry do not
+ * matter and are overwritten. Calls that overlap in time must not share a workspace.
+ *
+ *   q, o : [batch, heads_q, seqlen_q, head_dim] contiguous, dtype
+ *   k, v : [batch, heads_kv, seqlen_k, head_dim] contiguous, dtype
+ *   num_splits : key-range splits; 0 chooses about 1024 / (batch * heads_kv) (at least 1);
+ *                any value is clamped to [1, ceil(seqlen_k / tile)] with tile = 64 keys
+ *                (32 for fp32), and splits that would be empty are dropped
+ *
+ * batch == 0 or seqlen_q == 0 is an empty problem (AULE_OK, nothing launched). Besides the
+ * rules of aule_attn_fwd: (heads_q / heads_kv) * seqlen_q <= 64 query rows per kv head
+ * (AULE_ERR_UNSUPPORTED above that: use aule_attn_fwd), seqlen_q <= seqlen_k under causal
+ * (AULE_ERR_UNSUPPORTED), num_splits >= 0 and a large enough, aligned workspace
+ * (AULE_ERR_INVALID_ARGUMENT).
+ */
+aule_status_t aule_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                                    int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                    int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                    int32_t causal, float scale, aule_dtype_t dtype,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream);
+
+/*
+ * Workspace bytes aule_attn_fwd_splitkv needs for these arguments (a pure host computation;
+ * nothing is launched). Returns 0 for an empty problem and for arguments the call would
+ * reject (aule_last_error() then says why).
+ */
+size_t aule_attn_splitkv_workspace_size(int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                        int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                        aule_dtype_t dtype, int32_t num_splits);
 
 /* Static, NUL-terminated name of a status code. Never NULL. */
 const char* aule_status_string(aule_status_t status);

@@ -19,7 +19,7 @@ OK, INV, UNS = aule.AULE_OK, aule.AULE_ERR_INVALID_ARGUMENT, aule.AULE_ERR_UNSUP
 
 # distinct, 16-byte aligned, never dereferenced: each call below fails validation first
 P = {"q": 0x10000000, "k": 0x20000000, "v": 0x30000000, "o": 0x40000000,
-     "qkv": 0x50000000, "cu": 0x60000000}
+     "qkv": 0x50000000, "cu": 0x60000000, "ws": 0x70000000}
 
 
 @pytest.fixture(scope="module")
@@ -122,6 +122,53 @@ def test_varlen_empty_problem_is_noop(lib):
     assert varlen(total_tokens=0, qkv=None, cu=None, o=None) == OK
 
 
+def splitkv(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], o=P["o"], batch=2, heads_q=8, heads_kv=2,
+             seqlen_q=1, seqlen_k=1000, head_dim=128, causal=1, scale=0.088, dtype=BF16,
+             num_splits=0, ws=P["ws"], ws_bytes=1 << 24, stream=None)
+    a.update(kw)
+    return aule.aule_attn_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["batch"], a["heads_q"],
+                                      a["heads_kv"], a["seqlen_q"], a["seqlen_k"], a["head_dim"],
+                                      a["causal"], a["scale"], a["dtype"], a["num_splits"],
+                                      a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INV), (dict(k=None), INV), (dict(o=None), INV), (dict(ws=None), INV),
+    (dict(batch=-1), INV), (dict(seqlen_q=-1), INV), (dict(heads_kv=3), INV),
+    (dict(seqlen_k=0), INV), (dict(num_splits=-1), INV),
+    (dict(head_dim=136), UNS), (dict(head_dim=20), UNS), (dict(dtype=5), UNS),
+    (dict(seqlen_q=3, seqlen_k=2, causal=1), UNS),
+    (dict(seqlen_q=17, heads_q=8, heads_kv=2, causal=0), UNS),     # 4 * 17 > 64 rows
+    (dict(scale=math.nan), INV), (dict(ws=P["ws"] + 8), INV), (dict(ws_bytes=16), INV),
+    (dict(ws=P["q"]), INV), (dict(o=P["k"] + 16), INV),
+])
+def test_splitkv_rejects_invalid_arguments(lib, kw, status):
+    assert splitkv(**kw) == status
+    assert aule.aule_last_error() != ""
+
+
+def test_splitkv_empty_problems_are_noops(lib):
+    assert splitkv(batch=0, q=None, k=None, v=None, o=None, ws=None) == OK
+    assert splitkv(seqlen_q=0, q=None, k=None, v=None, o=None, ws=None) == OK
+
+
+def test_splitkv_workspace_size(lib):
+    ws = aule.aule_attn_splitkv_workspace_size
+    # 2 x 8 output rows; 1000 keys = 16 tiles of 64; explicit 4 splits of 4 tiles each:
+    # m, l rounded up to 256 bytes, then 4 x 16 x 128 floats
+    rows, s = 2 * 8 * 1, 4
+    assert ws(2, 8, 2, 1, 1000, 128, BF16, 4) == ((s * rows * 8 + 255) // 256 * 256) + s * rows * 128 * 4
+    # more splits than tiles are clamped; fp32 tiles are 32 keys
+    assert ws(1, 1, 1, 1, 64, 64, F16, 100) == 256 + 1 * 1 * 64 * 4
+    assert ws(1, 1, 1, 1, 64, 64, F32, 100) == 256 + 2 * 1 * 64 * 4
+    # automatic choice: about 1024 / (batch * heads_kv) splits, clamped to the tiles
+    assert ws(2, 8, 2, 1, 1 << 16, 64, BF16, 0) == ws(2, 8, 2, 1, 1 << 16, 64, BF16, 256)
+    # empty or rejected arguments -> 0
+    assert ws(0, 8, 2, 1, 100, 64, BF16, 0) == 0
+    assert ws(1, 8, 3, 1, 100, 64, BF16, 0) == 0 and aule.aule_last_error() != ""
+
+
 def test_python_wrappers_refuse_cpu_tensors(lib):
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
@@ -131,6 +178,8 @@ def test_python_wrappers_refuse_cpu_tensors(lib):
     cu = torch.tensor([0, 8], dtype=torch.int32)
     with pytest.raises(ValueError):
         aule.flash_attn_varlen_qkvpacked_func(qkv, cu, 8)
+    with pytest.raises(ValueError):
+        aule.flash_attention_decode(q, q, q)
     for kw in (dict(dropout_p=0.1), dict(window_size=(4, 4)), dict(softcap=1.0),
                dict(alibi_slopes=torch.zeros(2)), dict(return_attn_probs=True)):
         with pytest.raises(NotImplementedError):

@@ -15,7 +15,11 @@ wrappers follow the pages' APIs:
 * ``flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen, ...)`` — packed
   [total_tokens, 3, heads, head_dim] with cumulative ``cu_seqlens``, ``causal`` defaulting
   to False (ewbang.com article on a PyTorch FlashAttention for Turing, signature and
-  docstring of the varlen function; its unsupported options raise NotImplementedError).
+  docstring of the varlen function; its unsupported options raise NotImplementedError);
+* ``flash_attention_decode(q, k, v, causal=True, scale=None, num_splits=0)`` — a few new
+  queries against a key/value cache, split over the key range (FlashAttention-T
+  commentary, FAQ 4: the KV cache processed in blocks at inference); causal masking is
+  bottom-right aligned. The fp32 workspace is allocated with torch per call unless given.
 
 If the library is missing the import still succeeds, but every call raises: there is no
 CPU fallback.
@@ -33,7 +37,8 @@ LIB_PATH = os.environ.get("AULE_LIB") or os.path.join(_PKG, "libaule_attn.so")
 AULE_DTYPE_F32, AULE_DTYPE_F16, AULE_DTYPE_BF16 = 0, 1, 2
 AULE_OK, AULE_ERR_INVALID_ARGUMENT, AULE_ERR_UNSUPPORTED, AULE_ERR_HIP = 0, 1, 2, 3
 
-EXPORTED = ("aule_attn_fwd", "aule_attn_fwd_varlen", "aule_status_string", "aule_last_error")
+EXPORTED = ("aule_attn_fwd", "aule_attn_fwd_varlen", "aule_attn_fwd_splitkv",
+            "aule_attn_splitkv_workspace_size", "aule_status_string", "aule_last_error")
 
 _lib = None
 
@@ -61,6 +66,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.aule_attn_fwd_varlen.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                          ctypes.c_int, vp]
     lib.aule_attn_fwd_varlen.restype = ctypes.c_int
+    lib.aule_attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                          ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
+    lib.aule_attn_fwd_splitkv.restype = ctypes.c_int
+    lib.aule_attn_splitkv_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
+    lib.aule_attn_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.aule_status_string.argtypes = [ctypes.c_int]
     lib.aule_status_string.restype = ctypes.c_char_p
     lib.aule_last_error.argtypes = []
@@ -85,6 +95,23 @@ def aule_attn_fwd_varlen(qkv, cu_seqlens, o, num_seqs, total_tokens, max_seqlen,
     return load_library().aule_attn_fwd_varlen(qkv, cu_seqlens, o, num_seqs, total_tokens,
                                                max_seqlen, heads, head_dim, int(causal),
                                                float(scale), int(dtype), stream)
+
+
+def aule_attn_fwd_splitkv(q, k, v, o, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
+                          causal, scale, dtype, num_splits, workspace, workspace_bytes,
+                          stream=0) -> int:
+    """Raw call: device pointers as ints; returns the status code."""
+    return load_library().aule_attn_fwd_splitkv(q, k, v, o, batch, heads_q, heads_kv, seqlen_q,
+                                                seqlen_k, head_dim, int(causal), float(scale),
+                                                int(dtype), int(num_splits), workspace,
+                                                int(workspace_bytes), stream)
+
+
+def aule_attn_splitkv_workspace_size(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
+                                     dtype, num_splits=0) -> int:
+    return int(load_library().aule_attn_splitkv_workspace_size(batch, heads_q, heads_kv,
+                                                               seqlen_q, seqlen_k, head_dim,
+                                                               int(dtype), int(num_splits)))
 
 
 def aule_status_string(status: int) -> str:
@@ -156,6 +183,45 @@ def flash_attention(q, k, v, causal: bool = True, scale: float | None = None, ou
     return out
 
 
+def flash_attention_decode(q, k, v, causal: bool = True, scale: float | None = None,
+                           num_splits: int = 0, out=None, workspace=None):
+    """Attention of q [B,Hq,Nq,d] (a few new queries) against the cache k/v [B,Hkv,Nk,d],
+    split over the key range; under ``causal`` query i is position Nk - Nq + i. ``workspace``
+    (a uint8 GPU tensor of at least aule_attn_splitkv_workspace_size bytes) is allocated
+    here when not given."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need_gpu_tensor(name, t)
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [batch, heads, seq_len, head_dim]")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k and v must share a dtype")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("k and v must be [batch, heads_kv, seq_len_k, head_dim] matching q")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dt = dtype_code(q.dtype)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need_gpu_tensor("out", out)
+        if out.shape != q.shape or out.dtype != q.dtype:
+            raise ValueError("out must match q in shape and dtype")
+    need = aule_attn_splitkv_workspace_size(B, Hq, Hkv, Nq, Nk, d, dt, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    else:
+        _need_gpu_tensor("workspace", workspace)
+    st = aule_attn_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq,
+                               Hkv, Nq, Nk, d, causal, scale, dt, num_splits,
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                               _stream_handle(q.device))
+    _check(st)
+    return out
+
+
 def flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen, dropout_p=0.0,
                                      softmax_scale=None, causal=False, window_size=(-1, -1),
                                      softcap=0.0, alibi_slopes=None, deterministic=False,
@@ -206,6 +272,7 @@ def flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen, dropout_p=0.0,
     return out
 
 
-__all__ = ["aule_attn_fwd", "aule_attn_fwd_varlen", "aule_status_string", "aule_last_error",
-           "flash_attention", "flash_attn_varlen_qkvpacked_func", "load_library", "AuleError",
-           "LIB_PATH", "EXPORTED"]
+__all__ = ["aule_attn_fwd", "aule_attn_fwd_varlen", "aule_attn_fwd_splitkv",
+           "aule_attn_splitkv_workspace_size", "aule_status_string", "aule_last_error",
+           "flash_attention", "flash_attention_decode", "flash_attn_varlen_qkvpacked_func",
+           "load_library", "AuleError", "LIB_PATH", "EXPORTED"]

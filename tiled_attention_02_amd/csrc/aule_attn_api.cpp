@@ -11,6 +11,7 @@
 #include <cstdlib>
 
 #include "aule_attn.h"
+#include "attn_decode.h"
 #include "attn_problem.h"
 
 namespace {
@@ -70,6 +71,61 @@ aule_status_t dispatch(const aule::AttnProblem& p, aule_dtype_t dtype, hipStream
 }
 
 const float kLog2e = 1.4426950408889634f;
+
+// Split plan of the decoding path: how many key-range splits and how many keys each.
+struct SplitPlan {
+    int32_t splits;
+    int32_t keys_per_split;
+    size_t ml_bytes;   // workspace offset of the partial outputs (256-byte aligned)
+    size_t bytes;      // total workspace
+};
+
+constexpr int64_t kSplitTargetWorkgroups = 1024;   // about four per CU on a 256-CU device
+
+aule_status_t check_splitkv(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_q,
+                            int32_t seqlen_k, int32_t head_dim, int32_t causal, aule_dtype_t dtype,
+                            int32_t num_splits) {
+    if (batch < 0 || seqlen_q < 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "batch and seqlen_q must be >= 0");
+    if (num_splits < 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "num_splits must be >= 0 (got %d)", num_splits);
+    if (aule_status_t st = check_common(head_dim, 1.f, dtype)) return st;
+    if (heads_q <= 0 || heads_kv <= 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "heads_q and heads_kv must be positive");
+    if (heads_q % heads_kv != 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "heads_q (%d) must be a multiple of heads_kv (%d)", heads_q, heads_kv);
+    if (batch == 0 || seqlen_q == 0) return AULE_OK;
+    if (seqlen_k <= 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "seqlen_k must be positive for a non-empty problem");
+    if (causal && seqlen_q > seqlen_k)
+        return fail(AULE_ERR_UNSUPPORTED, "causal decoding needs seqlen_q <= seqlen_k (got %d, %d)", seqlen_q, seqlen_k);
+    if ((int64_t)(heads_q / heads_kv) * seqlen_q > 64)
+        return fail(AULE_ERR_UNSUPPORTED, "at most 64 query rows per kv head (got %d); use aule_attn_fwd",
+                    (heads_q / heads_kv) * seqlen_q);
+    if ((int64_t)batch * heads_q * seqlen_q > INT32_MAX)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "too many output rows");
+    if (batch > 65535 || heads_kv > 65535)   // grid z and y dimensions
+        return fail(AULE_ERR_UNSUPPORTED, "batch and heads_kv must be at most 65535 for split-KV decoding");
+    return AULE_OK;
+}
+
+SplitPlan plan_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_q,
+                      int32_t seqlen_k, int32_t head_dim, aule_dtype_t dtype, int32_t num_splits) {
+    const int64_t tk = aule::decode_keys_per_tile(static_cast<aule::Dtype>(dtype));
+    const int64_t tiles = (seqlen_k + tk - 1) / tk;
+    const int64_t groups = (int64_t)batch * heads_kv;
+    int64_t s = num_splits > 0 ? num_splits : (kSplitTargetWorkgroups + groups - 1) / groups;
+    s = s < 1 ? 1 : (s > tiles ? tiles : s);
+    const int64_t kps = (tiles + s - 1) / s * tk;           // whole tiles per split
+    s = (seqlen_k + kps - 1) / kps;                         // no empty split
+    const int64_t rows = (int64_t)batch * heads_q * seqlen_q;
+    SplitPlan pl;
+    pl.splits = (int32_t)s;
+    pl.keys_per_split = (int32_t)kps;
+    pl.ml_bytes = ((size_t)(s * rows * 2 * sizeof(float)) + 255) / 256 * 256;
+    pl.bytes = pl.ml_bytes + (size_t)(s * rows * head_dim) * sizeof(float);
+    return pl;
+}
 
 }  // namespace
 
@@ -168,6 +224,64 @@ aule_status_t aule_attn_fwd_varlen(const void* qkv, const int32_t* cu_seqlens, v
     p.total_tokens = total_tokens;
     p.max_seqlen = max_seqlen;
     return dispatch(p, dtype, stream);
+}
+
+aule_status_t aule_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                                    int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                    int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                    int32_t causal, float scale, aule_dtype_t dtype,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    if (aule_status_t st = check_splitkv(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
+                                         causal, dtype, num_splits))
+        return st;
+    if (!std::isfinite(scale))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (batch == 0 || seqlen_q == 0) {
+        g_last_error[0] = '\0';
+        return AULE_OK;  // empty problem
+    }
+    if (!q || !k || !v || !o || !workspace)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "tensor and workspace pointers must be 16-byte aligned");
+    const SplitPlan pl = plan_splits(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, dtype, num_splits);
+    if (workspace_bytes < pl.bytes)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu needed",
+                    workspace_bytes, pl.bytes);
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)batch * heads_q * seqlen_q * head_dim * es;
+    const size_t nkv = (size_t)batch * heads_kv * seqlen_k * head_dim * es;
+    if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "output overlaps an input");
+    if (overlaps(workspace, pl.bytes, q, nq) || overlaps(workspace, pl.bytes, k, nkv) ||
+        overlaps(workspace, pl.bytes, v, nkv) || overlaps(workspace, pl.bytes, o, nq))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "workspace overlaps a tensor");
+
+    aule::DecodeProblem p{};
+    p.q = q; p.k = k; p.v = v; p.o = o;
+    p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
+    p.seqlen_q = seqlen_q; p.seqlen_k = seqlen_k; p.head_dim = head_dim;
+    p.causal = causal ? 1 : 0;
+    p.scale = scale;
+    p.num_splits = pl.splits;
+    p.keys_per_split = pl.keys_per_split;
+    p.ws_ml = static_cast<float*>(workspace);
+    p.ws_o = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ml_bytes);
+    const hipError_t err = aule::launch_attn_decode(p, static_cast<aule::Dtype>(dtype), stream);
+    if (err != hipSuccess)
+        return fail(AULE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    g_last_error[0] = '\0';
+    return AULE_OK;
+}
+
+size_t aule_attn_splitkv_workspace_size(int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                        int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                        aule_dtype_t dtype, int32_t num_splits) {
+    if (check_splitkv(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, 0, dtype, num_splits) != AULE_OK)
+        return 0;
+    if (batch == 0 || seqlen_q == 0) return 0;
+    return plan_splits(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, dtype, num_splits).bytes;
 }
 
 const char* aule_status_string(aule_status_t status) {

@@ -183,6 +183,46 @@ class VarlenConfig:
         return qkv, cu
 
 
+@dataclass(frozen=True)
+class DecodeConfig:
+    """A few new queries per sequence against a key/value cache (causal: the queries are the
+    last seqlen_q positions, so query i sees keys j <= i + seqlen_k - seqlen_q)."""
+    name: str
+    dtype: str
+    batch: int
+    heads_q: int
+    heads_kv: int
+    seqlen_q: int
+    seqlen_k: int
+    head_dim: int
+    causal: bool
+    seed: int
+    sigma: float = 1.0
+    scale: float | None = None
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+
+    def pairs(self) -> int:
+        nq, nk = self.seqlen_q, self.seqlen_k
+        per = nq * (nk - nq) + nq * (nq + 1) // 2 if self.causal else nq * nk
+        return self.batch * per
+
+    def flops(self) -> int:
+        return 4 * self.head_dim * self.heads_q * self.pairs()
+
+    def bytes_compulsory(self) -> int:
+        """Q read and O written once, the K/V cache read once."""
+        e = {"f32": 4, "f16": 2, "bf16": 2}[self.dtype]
+        d, B = self.head_dim, self.batch
+        return e * d * B * (2 * self.heads_q * self.seqlen_q + 2 * self.heads_kv * self.seqlen_k)
+
+    def inputs(self):
+        return dense_inputs(self.batch, self.heads_q, self.heads_kv, self.seqlen_q, self.seqlen_k,
+                            self.head_dim, seed=self.seed, sigma=self.sigma, dtype=self.dtype)
+
+
 # The five workloads: a small fp32 case, the A10-shaped fp16 causal case, the bf16 causal
 # GQA case the throughput is quoted on, packed varlen, and a 32k long-context GQA case.
 CONFIGS = {
@@ -200,3 +240,10 @@ CONFIGS = {
 # Lengths the varlen workload must draw (regenerated and asserted in the tests).
 C4_LENGTHS = [3336, 409, 787, 1019, 795, 3295, 3569, 2411, 222, 443, 1403, 1810, 2569, 1996,
               1131, 708]
+
+# Decoding against a KV cache (the split-KV path): one new query per sequence, GQA, a
+# 16k-token bf16 cache of 512 MiB, so the step is bound by reading the cache from HBM.
+DECODE_CONFIGS = {
+    "d1_bf16_decode_gqa": DecodeConfig("d1_bf16_decode_gqa", "bf16", 8, 32, 8, 1, 16384, 128,
+                                       True, seed=6),
+}
