@@ -22,8 +22,12 @@
 //     r = w, w+4, ... (Q is held in LDS in fp32, pre-multiplied by scale * log2(e));
 //   * softmax: row max by a wave-wide reduction, P = exp2(s - m); each lane keeps its own
 //     partial row sum, reduced once at the end;
-//   * P V: lane l accumulates columns D/64 * l ... of the wave's rows, reading P back from
-//     LDS (one broadcast read per four keys) and one V element group per key.
+//   * scores (fp16/bf16): v_dot2 on packed pairs of K and raw Q, the scale applied to the
+//     finished dot product; (fp32): fp32 FMAs against Q pre-multiplied by the scale;
+//   * P V: lane l accumulates columns l and l + 64 of the wave's rows. fp16/bf16: P packed
+//     in pairs (RNE, the same rounded values summed into l), V^T read from LDS with the
+//     transposing ds_read_b64_tr_b16 (four keys of one column per lane), two v_dot2 per
+//     four keys; fp32: fp32 FMAs, P read back from LDS four keys at a time.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -33,7 +37,13 @@ namespace aule {
 namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -50,6 +60,14 @@ template <> struct Elem<bf16_t> {
     }
     static constexpr int kPerChunk = 8;
     static __device__ __forceinline__ bf16_t from_f32(float x) { return (bf16_t)x; }   // RNE
+    // acc + a.lo * b.lo + a.hi * b.hi over packed pairs, in fp32
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), acc, false);
+    }
+    // two fp32 -> packed pair, round to nearest even
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+    }
 };
 template <> struct Elem<f16_t> {
     static __device__ __forceinline__ void chunk(u32x4 c, float* f) {
@@ -61,6 +79,12 @@ template <> struct Elem<f16_t> {
     }
     static constexpr int kPerChunk = 8;
     static __device__ __forceinline__ f16_t from_f32(float x) { return (f16_t)x; }     // RNE
+    static __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float acc) {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, a), __builtin_bit_cast(f16x2, b), acc, false);
+    }
+    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+    }
 };
 template <> struct Elem<float> {
     static __device__ __forceinline__ void chunk(u32x4 c, float* f) {
@@ -101,11 +125,16 @@ __global__ __launch_bounds__(kThreads) void attn_decode_partial_kernel(DecodePro
     static_assert(NLD * kThreads == TILE_CHUNKS, "tile must split over the threads");
     static_assert(TK <= 64, "one lane per key");
 
-    // sQ and sP are read as 16-byte vectors: keep them 16-byte aligned
-    __shared__ __attribute__((aligned(16))) float sQ[RMAX][D];
+    constexpr bool HALF = sizeof(T) == 2;            // 16-bit path: dot2 on packed pairs
+    // Q rows: fp32 times scale * log2(e) (fp32 path) or the raw 16-bit chunks (16-bit path,
+    // the scale multiplies the finished dot product). P: fp32 (fp32 path) or packed pairs
+    // (16-bit path, the value that multiplies V). All read as vectors: 16-byte aligned.
+    __shared__ __attribute__((aligned(16))) float sQ[HALF ? 1 : RMAX][D];
+    __shared__ u32x4 sQh[HALF ? RMAX : 1][CPR];
     __shared__ u32x4 sK[TK * LDR];
     __shared__ u32x4 sV[TK * LDR];
-    __shared__ __attribute__((aligned(16))) float sP[RMAX][TK];
+    __shared__ __attribute__((aligned(16))) float sP[HALF ? 1 : RMAX][TK];
+    __shared__ __attribute__((aligned(16))) uint32_t sPh[HALF ? RMAX : 1][TK / 2];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -122,16 +151,30 @@ __global__ __launch_bounds__(kThreads) void attn_decode_partial_kernel(DecodePro
     // Q rows -> LDS as fp32 times scale * log2(e); row r = g * Nq + i is query i of head
     // hk * G + g
     const float c = p.scale * kLog2e;
-    for (int idx = tid; idx < RMAX * D; idx += kThreads) {
-        const int r = idx / D, col = idx % D;
-        float x = 0.f;
-        if (r < R && col < d) {
-            const int g = r / Nq, i = r - g * Nq;
-            const T* qrow = static_cast<const T*>(p.q) +
-                            (((int64_t)b * p.heads_q + hk * G + g) * Nq + i) * d;
-            x = static_cast<float>(qrow[col]);
+    if constexpr (HALF) {
+        for (int idx = tid; idx < RMAX * CPR; idx += kThreads) {
+            const int r = idx / CPR, cc = idx % CPR;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (r < R && cc * EPC < d) {
+                const int g = r / Nq, i = r - g * Nq;
+                const T* qrow = static_cast<const T*>(p.q) +
+                                (((int64_t)b * p.heads_q + hk * G + g) * Nq + i) * d;
+                x = *reinterpret_cast<const u32x4*>(qrow + cc * EPC);
+            }
+            sQh[r][cc] = x;
         }
-        sQ[r][col] = x * c;
+    } else {
+        for (int idx = tid; idx < RMAX * D; idx += kThreads) {
+            const int r = idx / D, col = idx % D;
+            float x = 0.f;
+            if (r < R && col < d) {
+                const int g = r / Nq, i = r - g * Nq;
+                const T* qrow = static_cast<const T*>(p.q) +
+                                (((int64_t)b * p.heads_q + hk * G + g) * Nq + i) * d;
+                x = static_cast<float>(qrow[col]);
+            }
+            sQ[r][col] = x * c;
+        }
     }
 
     const T* kbase = static_cast<const T*>(p.k) + ((int64_t)b * p.heads_kv + hk) * (int64_t)Nk * d;
@@ -182,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_partial_kernel(DecodePro
         __syncthreads();                              // tile visible (and sQ, first time)
         if (k0 + TK < k_end) fetch(k0 + TK);          // next tile in flight during compute
 
-        // ---- scores: lane = key of the tile, wave rows r = wave + 4q
+        // ---- scores: lane = key of the tile, wave rows r = wave + 4q (in log2 units)
         const int key = k0 + lane;
         float s[RPW];
 #pragma unroll
@@ -190,26 +233,41 @@ __global__ __launch_bounds__(kThreads) void attn_decode_partial_kernel(DecodePro
         if (lane < TK) {
 #pragma unroll 4
             for (int cc = 0; cc < CPR; ++cc) {
-                float kf[EPC];
-                Elem<T>::chunk(sK[lane * LDR + cc], kf);
+                const u32x4 kc = sK[lane * LDR + cc];
+                if constexpr (HALF) {
 #pragma unroll
-                for (int q = 0; q < RPW; ++q) {
-                    const int r = wave + 4 * q;
-                    if (r < R) {
-                        const f32x4* qv = reinterpret_cast<const f32x4*>(&sQ[r][cc * EPC]);
+                    for (int q = 0; q < RPW; ++q) {
+                        const int r = wave + 4 * q;
+                        if (r < R) {
+                            const u32x4 qc = sQh[r][cc];
 #pragma unroll
-                        for (int e4 = 0; e4 < EPC / 4; ++e4) {
-                            const f32x4 qq = qv[e4];
-                            s[q] = fmaf(kf[4 * e4], qq[0], s[q]);
-                            s[q] = fmaf(kf[4 * e4 + 1], qq[1], s[q]);
-                            s[q] = fmaf(kf[4 * e4 + 2], qq[2], s[q]);
-                            s[q] = fmaf(kf[4 * e4 + 3], qq[3], s[q]);
+                            for (int w = 0; w < 4; ++w) s[q] = Elem<T>::dot2(kc[w], qc[w], s[q]);
+                        }
+                    }
+                } else {
+                    float kf[EPC];
+                    Elem<T>::chunk(kc, kf);
+#pragma unroll
+                    for (int q = 0; q < RPW; ++q) {
+                        const int r = wave + 4 * q;
+                        if (r < R) {
+                            const f32x4 qq = *reinterpret_cast<const f32x4*>(&sQ[r][cc * EPC]);
+                            s[q] = fmaf(kf[0], qq[0], s[q]);
+                            s[q] = fmaf(kf[1], qq[1], s[q]);
+                            s[q] = fmaf(kf[2], qq[2], s[q]);
+                            s[q] = fmaf(kf[3], qq[3], s[q]);
                         }
                     }
                 }
             }
+            if constexpr (HALF) {
+#pragma unroll
+                for (int q = 0; q < RPW; ++q) s[q] *= c;
+            }
         }
-        // ---- online softmax per row (wave-uniform branches)
+        // ---- online softmax per row (wave-uniform branches). 16-bit path: P is packed in
+        // pairs of neighbouring keys (even lanes store), and the row sum is taken over the
+        // rounded pairs, so l matches the P that multiplies V.
 #pragma unroll
         for (int q = 0; q < RPW; ++q) {
             const int r = wave + 4 * q;
@@ -227,31 +285,68 @@ __global__ __launch_bounds__(kThreads) void attn_decode_partial_kernel(DecodePro
                 for (int e = 0; e < CPL; ++e) o[q][e] *= alpha;
                 m[q] = m_new;
             }
-            lpart[q] += pj;
-            if (lane < TK) sP[r][lane] = pj;
-        }
-        // ---- O += P V: lane owns columns CPL * lane ...; P read back four keys at a time
-        // (each wave reads only the rows it wrote, so no barrier is needed in between)
-#pragma unroll 2
-        for (int j4 = 0; j4 < TK; j4 += 4) {
-            float vv[4][CPL];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j = j4 + jj;
-                const int col0 = CPL * lane;                       // element column
-                const T* vr = reinterpret_cast<const T*>(&sV[j * LDR + col0 / EPC]) + col0 % EPC;
-#pragma unroll
-                for (int e = 0; e < CPL; ++e) vv[jj][e] = static_cast<float>(vr[e]);
+            if constexpr (HALF) {
+                const float pn = __shfl_xor(pj, 1);
+                if ((lane & 1) == 0 && lane < TK) {
+                    const uint32_t pk = Elem<T>::pack2(pj, pn);
+                    sPh[r][lane >> 1] = pk;
+                    lpart[q] = Elem<T>::dot2(pk, Elem<T>::pack2(1.f, 1.f), lpart[q]);
+                }
+            } else {
+                lpart[q] += pj;
+                if (lane < TK) sP[r][lane] = pj;
             }
+        }
+        // ---- O += P V; lane owns columns lane + 64 e. Each wave reads only the P rows it
+        // wrote, so no barrier is needed in between.
+        if constexpr (HALF) {
+            // V^T from the row-major V tile: each 16-lane group reads a 4-key x 16-column
+            // block transposed (lane c addresses key c/4, columns 4(c%4)..+3; lane i gets
+            // the 4 keys of column i), then two dot2 against the matching P pairs.
+            const int tg = lane >> 4, tc = lane & 15;
+#pragma unroll 4
+            for (int j4 = 0; j4 < TK; j4 += 4) {
+                u32x2 vt[CPL];
 #pragma unroll
-            for (int q = 0; q < RPW; ++q) {
-                const int r = wave + 4 * q;
-                if (r >= R) continue;
-                const f32x4 pp = *reinterpret_cast<const f32x4*>(&sP[r][j4]);
+                for (int e = 0; e < CPL; ++e) {
+                    const int col = 64 * e + 16 * tg + 4 * (tc & 3);
+                    const char* addr = reinterpret_cast<const char*>(&sV[(j4 + (tc >> 2)) * LDR + col / EPC]) +
+                                       (col % EPC) * sizeof(T);
+                    const i16x4_t part = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<char*>(addr)));
+                    vt[e] = __builtin_bit_cast(u32x2, part);
+                }
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj)
+                for (int q = 0; q < RPW; ++q) {
+                    const int r = wave + 4 * q;
+                    if (r >= R) continue;
+                    const u32x2 pp = *reinterpret_cast<const u32x2*>(&sPh[r][j4 >> 1]);
 #pragma unroll
-                    for (int e = 0; e < CPL; ++e) o[q][e] = fmaf(pp[jj], vv[jj][e], o[q][e]);
+                    for (int e = 0; e < CPL; ++e) {
+                        o[q][e] = Elem<T>::dot2(vt[e][0], pp[0], o[q][e]);
+                        o[q][e] = Elem<T>::dot2(vt[e][1], pp[1], o[q][e]);
+                    }
+                }
+            }
+        } else {
+#pragma unroll 2
+            for (int j4 = 0; j4 < TK; j4 += 4) {
+                float vv[4][CPL];
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const float* vr = reinterpret_cast<const float*>(&sV[(j4 + jj) * LDR]);
+#pragma unroll
+                    for (int e = 0; e < CPL; ++e) vv[jj][e] = vr[lane + 64 * e];
+                }
+#pragma unroll
+                for (int q = 0; q < RPW; ++q) {
+                    const int r = wave + 4 * q;
+                    if (r >= R) continue;
+                    const f32x4 pp = *reinterpret_cast<const f32x4*>(&sP[r][j4]);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+                        for (int e = 0; e < CPL; ++e) o[q][e] = fmaf(pp[jj], vv[jj][e], o[q][e]);
+                }
             }
         }
     }
@@ -272,40 +367,59 @@ __global__ __launch_bounds__(kThreads) void attn_decode_partial_kernel(DecodePro
         }
 #pragma unroll
         for (int e = 0; e < CPL; ++e) {
-            const int col = CPL * lane + e;
+            const int col = lane + 64 * e;
             if (col < d) p.ws_o[slot * d + col] = o[q][e];
         }
     }
 }
 
 // Merge the splits of one output row: m = max m_s, l = sum l_s 2^(m_s - m),
-// O = sum O_s 2^(m_s - m) / l. One workgroup of 64 threads per (batch, head, query) row.
+// O = sum O_s 2^(m_s - m) / l. One wave per (batch, head, query) row: lane s holds split s's
+// statistics (64 splits at a time), the weights go through wave reductions, and the
+// partial outputs of all splits are loaded independently (columns lane and lane + 64).
 template <typename T>
 __global__ __launch_bounds__(64) void attn_decode_combine_kernel(DecodeProblem p) {
     const int64_t row = blockIdx.x;
     const int64_t rows_total = (int64_t)p.batch * p.heads_q * p.seqlen_q;
     const int d = p.head_dim;
+    const int lane = threadIdx.x;
+    const int S = p.num_splits;
     float mx = -INFINITY;
-    for (int s = 0; s < p.num_splits; ++s) mx = fmaxf(mx, p.ws_ml[2 * (s * rows_total + row)]);
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        const int s = s0 + lane;
+        const float ms = s < S ? p.ws_ml[2 * (s * rows_total + row)] : -INFINITY;
+        mx = fmaxf(mx, wave_max(ms));
+    }
     float l = 0.f;
     float acc[2] = {0.f, 0.f};
-    for (int s = 0; s < p.num_splits; ++s) {
-        const int64_t slot = s * rows_total + row;
-        const float ms = p.ws_ml[2 * slot];
-        if (ms == -INFINITY) continue;              // a split with no visible key
-        const float w = __builtin_amdgcn_exp2f(ms - mx);
-        l = fmaf(p.ws_ml[2 * slot + 1], w, l);
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        const int s = s0 + lane;
+        float w = 0.f;
+        if (s < S) {
+            const int64_t slot = s * rows_total + row;
+            const float ms = p.ws_ml[2 * slot];
+            // a split without any visible key has m = -inf and weight 0
+            w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - mx);
+            l = fmaf(p.ws_ml[2 * slot + 1], w, l);
+        }
+        const int n = min(64, S - s0);
+#pragma unroll 8
+        for (int j = 0; j < n; ++j) {
+            const float wj = __shfl(w, j);
+            const int64_t slot = (int64_t)(s0 + j) * rows_total + row;
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            const int col = threadIdx.x + 64 * e;
-            if (col < d) acc[e] = fmaf(p.ws_o[slot * d + col], w, acc[e]);
+            for (int e = 0; e < 2; ++e) {
+                const int col = lane + 64 * e;
+                if (col < d) acc[e] = fmaf(p.ws_o[slot * d + col], wj, acc[e]);
+            }
         }
     }
+    l = wave_sum(l);
     const float inv = 1.f / l;
     T* orow = static_cast<T*>(p.o) + row * d;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int col = threadIdx.x + 64 * e;
+        const int col = lane + 64 * e;
         if (col < d) orow[col] = Elem<T>::from_f32(acc[e] * inv);
     }
 }
