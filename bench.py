@@ -24,35 +24,50 @@ sys.path.insert(0, ROOT)
 
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}   # MI355X dense, published
 HBM_PEAK_GBS = 8000.0
+# Sources each workload's kernels are built from: a traffic record taken on other sources is
+# stale and not reported.
 KERNEL_SOURCES = ["tiled_attention_02_amd/csrc/attn_fwd_mfma.hip",
                   "tiled_attention_02_amd/csrc/attn_device.h",
                   "tiled_attention_02_amd/csrc/attn_problem.h",
                   "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
+DECODE_SOURCES = ["tiled_attention_02_amd/csrc/attn_decode.hip",
+                  "tiled_attention_02_amd/csrc/attn_decode.h",
+                  "tiled_attention_02_amd/csrc/attn_device.h",
+                  "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
+def sources_for(workload):
+    return DECODE_SOURCES if workload.startswith("d") else KERNEL_SOURCES
+
+
 def measured_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE record, scaled
-    by the copy-kernel calibration; None when the record is absent, for another workload, or
-    taken on kernel sources that have changed since."""
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE record of
+    this workload, scaled by the copy-kernel calibration and summed over the launch's
+    kernels; None when there is no record for the workload or it was taken on kernel
+    sources that have changed since."""
     try:
         with open(TRAFFIC_RECORD) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            records = json.load(f)["records"]
+    except (OSError, ValueError, KeyError):
         return None
-    if rec.get("workload") != workload or rec.get("kernel_source_sha") != kernel_source_hash():
-        return None
-    kib = rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]
-    return int(kib * 1024)
+    for rec in records:
+        if rec.get("workload") != workload:
+            continue
+        if rec.get("kernel_source_sha") != kernel_source_hash(sources_for(workload)):
+            return None
+        kib = rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]
+        return int(kib * 1024)
+    return None
 
 
 def parse():
@@ -67,7 +82,7 @@ def parse():
     ap.add_argument("--all", action="store_true",
                     help="also time every workload and report them on stderr")
     ap.add_argument("--print-kernel-hash", action="store_true",
-                    help="print the hash of the kernel sources the traffic record is keyed to")
+                    help="print the hash of the kernel sources the workload's traffic record is keyed to")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -203,7 +218,7 @@ def cpu_baseline(cfg, host_inputs, budget_s):
 def main():
     args = parse()
     if args.print_kernel_hash:
-        print(kernel_source_hash())
+        print(kernel_source_hash(sources_for(args.workload)))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this library has no multi-GPU path "
