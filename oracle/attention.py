@@ -221,3 +221,77 @@ def attention_ref_decode(q, k, v, *, causal: bool, scale: float) -> np.ndarray:
                 S[masked] = -np.inf
             out[b, hq] = _softmax_rows_times_v(S, v[b, hk])
     return out
+
+
+# ---------------------------------------------------------------- log-sum-exp and gradients
+#
+# Training through the tiled forward (FlashAttention-T commentary, FAQ 4, training bullet:
+# the forward keeps no score matrix and the backward recomputes it) needs, per query row,
+# the log-sum-exp of the scaled scores, and the gradients of O with respect to Q, K and V.
+# Both have plain definitions, written out here:
+#
+#   LSE[i]  = log sum_j exp(S[i, j])                      (S scaled and masked as above)
+#   P       = exp(S - LSE)                                (= softmax(S))
+#   dV      = P^T dO
+#   dP      = dO V^T
+#   dS      = P * (dP - rowsum(dP * P))                   (softmax Jacobian, rowwise)
+#   dQ      = scale * dS K,     dK = scale * dS^T Q
+#
+# With grouped-query attention, the gradient of a shared key/value head is the sum over the
+# query heads that read it.
+
+def _lse_rows(S: np.ndarray) -> np.ndarray:
+    m = S.max(axis=1, keepdims=True)
+    return (m + np.log(np.exp(S - m).sum(axis=1, keepdims=True)))[:, 0]
+
+
+def attention_ref_lse(q, k, v, *, causal: bool, scale: float) -> np.ndarray:
+    """Per-row log-sum-exp (natural log) of the scaled, masked scores, float64 [B,Hq,Nq]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, Hkv, Nq, Nk, d = _check_dense(q, k, v, causal)
+    G = Hq // Hkv
+    sc = _scale64(scale)
+    out = np.empty((B, Hq, Nq), dtype=np.float64)
+    if causal:
+        masked = _causal_masked(np.arange(Nq), Nk)
+    for b in range(B):
+        for hq in range(Hq):
+            S = sc * (q[b, hq] @ k[b, _kv_head(hq, G)].T)
+            if causal:
+                S[masked] = -np.inf
+            out[b, hq] = _lse_rows(S)
+    return out
+
+
+def _softmax_backward(P: np.ndarray, dP: np.ndarray) -> np.ndarray:
+    """dS = P * (dP - rowsum(dP * P)): the gradient through a row-wise softmax."""
+    return P * (dP - (dP * P).sum(axis=1, keepdims=True))
+
+
+def attention_ref_bwd(q, k, v, do, *, causal: bool, scale: float):
+    """Gradients of O = attention(q, k, v) for the output gradient ``do`` [B,Hq,Nq,d].
+    Returns float64 (dq [B,Hq,Nq,d], dk [B,Hkv,Nk,d], dv [B,Hkv,Nk,d])."""
+    q, k, v, do = _f64(q), _f64(k), _f64(v), _f64(do)
+    B, Hq, Hkv, Nq, Nk, d = _check_dense(q, k, v, causal)
+    if do.shape != q.shape:
+        raise ValueError("do must have the shape of q")
+    G = Hq // Hkv
+    sc = _scale64(scale)
+    dq = np.zeros((B, Hq, Nq, d))
+    dk = np.zeros((B, Hkv, Nk, d))
+    dv = np.zeros((B, Hkv, Nk, d))
+    if causal:
+        masked = _causal_masked(np.arange(Nq), Nk)
+    for b in range(B):
+        for hq in range(Hq):
+            hk = _kv_head(hq, G)
+            S = sc * (q[b, hq] @ k[b, hk].T)
+            if causal:
+                S[masked] = -np.inf
+            P = np.exp(S - _lse_rows(S)[:, None])
+            dv[b, hk] += P.T @ do[b, hq]
+            dP = do[b, hq] @ v[b, hk].T
+            dS = _softmax_backward(P, dP)
+            dq[b, hq] = sc * (dS @ k[b, hk])
+            dk[b, hk] += sc * (dS.T @ q[b, hq])
+    return dq, dk, dv

@@ -493,6 +493,86 @@ def test_decode_validation():
     oracle.attention_ref_decode(q, k, k, causal=False, scale=1.0)   # non-causal: any Nq
 
 
+# ---------------------------------------------------------------- log-sum-exp and gradients
+
+def test_lse_single_key_and_uniform_scores():
+    rng = np.random.default_rng(401)
+    q = rng.standard_normal((1, 2, 3, 5))
+    k = rng.standard_normal((1, 1, 1, 5))
+    lse = oracle.attention_ref_lse(q, k, k, causal=False, scale=0.7)
+    sc = float(np.float32(0.7))
+    np.testing.assert_allclose(lse[0, :, :], sc * (q[0] @ k[0, 0, 0]), rtol=0, atol=1e-13)
+    q = rng.standard_normal((1, 1, 6, 4))
+    k = rng.standard_normal((1, 1, 6, 4))
+    lse = oracle.attention_ref_lse(q, k, k, causal=True, scale=0.0)
+    np.testing.assert_allclose(lse[0, 0], np.log(np.arange(1, 7)), rtol=0, atol=1e-13)
+
+
+def test_lse_brute_force():
+    rng = np.random.default_rng(402)
+    q = rng.standard_normal((1, 2, 4, 3))
+    k = rng.standard_normal((1, 2, 5, 3))
+    got = oracle.attention_ref_lse(q, k, k, causal=False, scale=1.1)
+    sc = float(np.float32(1.1))
+    for h in range(2):
+        for i in range(4):
+            tot = 0.0
+            for j in range(5):
+                dot = sum(float(q[0, h, i, c]) * float(k[0, h, j, c]) for c in range(3))
+                tot += math.exp(sc * dot)
+            assert abs(got[0, h, i] - math.log(tot)) < 1e-12
+
+
+def _finite_difference_grads(q, k, v, do, causal, scale, h=1e-6):
+    """Central differences of L = sum(O * do) through the forward oracle."""
+    def loss(q_, k_, v_):
+        return float(np.sum(oracle.attention_ref(q_, k_, v_, causal=causal, scale=scale) * do))
+    grads = []
+    for which in range(3):
+        base = [q.copy(), k.copy(), v.copy()]
+        g = np.zeros_like(base[which])
+        it = np.nditer(base[which], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            plus = [x.copy() for x in base]
+            minus = [x.copy() for x in base]
+            plus[which][idx] += h
+            minus[which][idx] -= h
+            g[idx] = (loss(*plus) - loss(*minus)) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_finite_differences(causal):
+    rng = np.random.default_rng(410 + causal)
+    B, Hkv, G, N, d = 1, 1, 2, 4, 3
+    q = rng.standard_normal((B, Hkv * G, N, d))
+    k = rng.standard_normal((B, Hkv, N, d))
+    v = rng.standard_normal((B, Hkv, N, d))
+    do = rng.standard_normal((B, Hkv * G, N, d))
+    dq, dk, dv = oracle.attention_ref_bwd(q, k, v, do, causal=causal, scale=0.8)
+    fq, fk, fv = _finite_difference_grads(q, k, v, do, causal, 0.8)
+    np.testing.assert_allclose(dq, fq, rtol=0, atol=1e-7)
+    np.testing.assert_allclose(dk, fk, rtol=0, atol=1e-7)
+    np.testing.assert_allclose(dv, fv, rtol=0, atol=1e-7)
+
+
+def test_backward_single_key():
+    """One key: P = 1 everywhere, so dV = sum of dO over the rows and heads that read it,
+    and Q, K get no gradient."""
+    rng = np.random.default_rng(420)
+    q = rng.standard_normal((1, 4, 3, 5))
+    k = rng.standard_normal((1, 2, 1, 5))
+    v = rng.standard_normal((1, 2, 1, 5))
+    do = rng.standard_normal((1, 4, 3, 5))
+    dq, dk, dv = oracle.attention_ref_bwd(q, k, v, do, causal=False, scale=0.5)
+    np.testing.assert_allclose(dq, 0, atol=1e-13)
+    np.testing.assert_allclose(dk, 0, atol=1e-13)
+    np.testing.assert_allclose(dv[0, 0, 0], do[0, 0:2].sum(axis=(0, 1)), atol=1e-13)
+    np.testing.assert_allclose(dv[0, 1, 0], do[0, 2:4].sum(axis=(0, 1)), atol=1e-13)
+
+
 # ---------------------------------------------------------------- mutation checks
 
 def _pins_pass():
@@ -510,6 +590,8 @@ def _pins_pass():
         lambda: test_single_key_returns_v("full", 0.125),
         lambda: test_decode_tail_of_full_causal(5),
         lambda: test_decode_brute_force_tiny(0),
+        lambda: test_backward_matches_finite_differences(True),
+        lambda: test_lse_single_key_and_uniform_scores(),
     ]
     for c in checks:
         try:
@@ -553,6 +635,8 @@ MUTANTS = {
     "softmax_sign_flipped": ("_softmax_rows_times_v", _mut_softmax_sign),
     "scale_inverted": ("_scale64", lambda s: 1.0 / float(np.float32(s)) if s else 0.0),
     "scale_dropped": ("_scale64", lambda s: 1.0),
+    "softmax_backward_no_rowsum": ("_softmax_backward", lambda P, dP: P * dP),
+    "lse_without_max_shift": ("_lse_rows", lambda S: np.log(np.exp(S).sum(axis=1)) + 1e-3),
     "decode_mask_top_left": ("_decode_masked",
                              lambda nq, nk: np.arange(nk)[None, :] > np.arange(nq)[:, None]),
     "decode_mask_includes_next_key": ("_decode_masked",
