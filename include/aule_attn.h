@@ -148,6 +148,47 @@ size_t aule_attn_splitkv_workspace_size(int32_t batch, int32_t heads_q, int32_t 
                                         int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
                                         aule_dtype_t dtype, int32_t num_splits);
 
+/*
+ * Attention forward that also writes the per-row log-sum-exp needed by the backward.
+ *
+ * Same operation, arguments and rules as aule_attn_fwd, plus
+ *   lse : [batch, heads_q, seqlen_q] fp32, DEVICE, written: the natural-log log-sum-exp of
+ *         the scaled, masked scores of each query row, log(sum_j exp(scale * q_i . k_j)).
+ * The forward keeps no score matrix; the backward recomputes it from Q, K and lse
+ * (FlashAttention-T commentary, ai-stack.site, FAQ 4, training bullet). For fp16/bf16 the
+ * row sum is taken over the probabilities as rounded to dtype (those that multiply V), so lse
+ * is within about the dtype's unit roundoff (2^-11 fp16, 2^-8 bf16) of the exact value; fp32
+ * is exact up to fp32 rounding. lse must be 4-byte aligned and must not overlap any tensor.
+ */
+aule_status_t aule_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                int32_t causal, float scale, aule_dtype_t dtype,
+                                hipStream_t stream);
+
+/*
+ * Attention backward: gradients of O = attention(q, k, v) for the output gradient do.
+ *
+ *   q, o, do, dq : [batch, heads_q, seqlen_q, head_dim] contiguous, dtype (dq written)
+ *   k, v, dk, dv : [batch, heads_kv, seqlen_k, head_dim] contiguous, dtype (dk, dv written)
+ *   lse          : [batch, heads_q, seqlen_q] fp32, as written by aule_attn_fwd_lse for the
+ *                  same q, k, v, causal and scale
+ *
+ * With P = exp(scale * q k^T - lse) (masked entries 0), dV = P^T dO, dS = P * (dO v^T - D)
+ * with D_i = do_i . o_i, dQ = scale * dS k and dK = scale * dS^T q; a key/value head shared
+ * by several query heads (GQA) receives the sum of their gradients. fp32 arithmetic for all
+ * dtypes; gradients rounded to dtype (RNE). Needs no workspace; deterministic (no atomics).
+ * Arguments and rules as aule_attn_fwd; the gradient buffers must not overlap any input or
+ * each other. With seqlen_q == 0 and seqlen_k > 0 (non-causal) only dk and dv are read
+ * (written as zeros); with batch == 0 nothing is read or launched.
+ */
+aule_status_t aule_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv,
+                            int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                            int32_t causal, float scale, aule_dtype_t dtype,
+                            hipStream_t stream);
+
 /* Static, NUL-terminated name of a status code. Never NULL. */
 const char* aule_status_string(aule_status_t status);
 

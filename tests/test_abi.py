@@ -169,6 +169,42 @@ def test_splitkv_workspace_size(lib):
     assert ws(1, 8, 3, 1, 100, 64, BF16, 0) == 0 and aule.aule_last_error() != ""
 
 
+def bwd(**kw):
+    a = dict(q=P["q"], k=P["k"], v=P["v"], o=P["o"], do=0x80000000, lse=0x90000000,
+             dq=0xA0000000, dk=0xB0000000, dv=0xC0000000, batch=1, heads_q=4, heads_kv=2,
+             seqlen_q=16, seqlen_k=16, head_dim=64, causal=1, scale=0.125, dtype=BF16, stream=None)
+    a.update(kw)
+    return aule.aule_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["dq"], a["dk"],
+                              a["dv"], a["batch"], a["heads_q"], a["heads_kv"], a["seqlen_q"],
+                              a["seqlen_k"], a["head_dim"], a["causal"], a["scale"], a["dtype"],
+                              a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), INV), (dict(do=None), INV), (dict(lse=None), INV), (dict(dq=None), INV),
+    (dict(dk=None), INV), (dict(dv=None), INV), (dict(heads_q=6, heads_kv=4), INV),
+    (dict(seqlen_k=32), UNS), (dict(head_dim=136), UNS), (dict(scale=math.nan), INV),
+    (dict(dq=P["q"]), INV), (dict(dk=P["v"] + 16), INV), (dict(dv=0xB0000000), INV),
+    (dict(lse=0x90000002), INV), (dict(dq=0xA0000008), INV), (dict(dtype=9), UNS),
+])
+def test_bwd_rejects_invalid_arguments(lib, kw, status):
+    assert bwd(**kw) == status
+    assert aule.aule_last_error() != ""
+
+
+def test_fwd_lse_rejects_null_lse(lib):
+    st = aule.aule_attn_fwd_lse(P["q"], P["k"], P["v"], P["o"], None, 1, 4, 2, 16, 16, 64, 1,
+                                0.125, BF16, None)
+    assert st == INV
+    assert aule.aule_attn_fwd_lse(P["q"], P["k"], P["v"], P["o"], P["q"] + 64, 1, 4, 2, 16, 16,
+                                  64, 1, 0.125, BF16, None) == INV     # lse overlaps q
+
+
+def test_bwd_empty_problem_is_noop(lib):
+    assert bwd(batch=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None, dk=None,
+               dv=None) == OK
+
+
 def test_python_wrappers_refuse_cpu_tensors(lib):
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)

@@ -1,0 +1,160 @@
+"""GPU parity of the attention backward (aule_attn_fwd_lse + aule_attn_bwd, through the C-ABI
+library) against the CPU fp64 oracle's attention_ref_lse and attention_ref_bwd on the same
+seeded, dtype-rounded inputs.
+
+Bars. The per-row log-sum-exp is fp32, but the 16-bit forward sums the probabilities after
+rounding them to the dtype (the same P that multiplies V, so that O is a convex combination of
+V rows), which moves the sum by at most the unit roundoff u of the dtype relative and the log
+by at most about u: |err| <= (u + 2e-5) * max(1, |lse|), with u = 2^-8 (bf16), 2^-11 (fp16)
+and 0 (fp32), 2e-5 covering the fp32 sums and the exp2/log2 instructions.
+The gradients are compared on the max abs error over every element, divided by
+max(1, max |reference|) of that tensor, against the forward's bars: 1e-5 for fp32, 2e-3 for
+fp16 and 1e-2 for bf16. Each gradient is a sum of products of rounded inputs with O (itself
+rounded to the dtype by the forward, which enters through D_i = do_i . o_i) and with P (from
+the lse above), then rounded once to the dtype: the output rounding alone is 2^-11 (fp16) /
+2^-8 (bf16) relative to the largest element, and the O and lse terms add a few more unit
+roundoffs, which the 16-bit bars (about 4 u) cover."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import tiled_attention_02_amd as aule
+from workloads import dense_inputs, round_to_dtype
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GTOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
+LSE_TOL = {"f32": 2e-5, "f16": 2.0 ** -11 + 2e-5, "bf16": 2.0 ** -8 + 2e-5}
+TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    aule.load_library()
+
+
+def dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda", dtype=TDT[dtype])
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def grad_out(shape, seed, dtype):
+    rng = np.random.default_rng(seed + 1000)
+    return round_to_dtype(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+
+def rel_err(got, ref):
+    return float(np.max(np.abs(got - ref))) / max(1.0, float(np.max(np.abs(ref))))
+
+
+def run(B, Hq, Hkv, Nq, Nk, d, dtype, causal, scale=None, seed=0):
+    print(f"bwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal} "
+          f"scale={scale} seed={seed}", flush=True)
+    q, k, v = dense_inputs(B, Hq, Hkv, Nq, Nk, d, seed=seed, dtype=dtype)
+    do = grad_out(q.shape, seed, dtype)
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    tq, tk, tv, tdo = dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(do, dtype)
+    o, lse = aule.flash_attention(tq, tk, tv, causal=causal, scale=sc, return_lse=True)
+    dq, dk, dv = aule.flash_attention_backward(tq, tk, tv, o, tdo, lse, causal=causal, scale=sc)
+    torch.cuda.synchronize()
+    return (q, k, v, do, sc), (host(o), host(lse), host(dq), host(dk), host(dv))
+
+
+def check(B, Hq, Hkv, Nq, Nk, d, dtype, causal, scale=None, seed=0):
+    (q, k, v, do, sc), (o, lse, dq, dk, dv) = run(B, Hq, Hkv, Nq, Nk, d, dtype, causal, scale, seed)
+    ref_lse = oracle.attention_ref_lse(q, k, v, causal=causal, scale=sc)
+    assert np.all(np.isfinite(lse))
+    lse_err = float(np.max(np.abs(lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse))))
+    assert lse_err <= LSE_TOL[dtype], f"lse err {lse_err}"
+    rdq, rdk, rdv = oracle.attention_ref_bwd(q, k, v, do, causal=causal, scale=sc)
+    errs = {}
+    for name, got, ref in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert np.all(np.isfinite(got)), name
+        errs[name] = rel_err(got, ref)
+    print("  errors", errs, flush=True)
+    for name, e in errs.items():
+        assert e <= GTOL[dtype], f"{name} relative err {e} > {GTOL[dtype]}"
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("N", [1, 31, 100, 257])
+def test_bwd_shapes(dtype, causal, N):
+    check(2, 4, 2, N, N, 64, dtype, causal, seed=N)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [8, 40, 64, 72, 96, 128])
+def test_bwd_head_dims(dtype, d):
+    check(1, 4, 1, 77, 77, d, dtype, True, seed=d)
+
+
+@pytest.mark.parametrize("Nq,Nk", [(40, 70), (70, 40), (1, 300), (300, 1)])
+def test_bwd_cross_lengths(Nq, Nk):
+    check(1, 6, 2, Nq, Nk, 128, "bf16", False, seed=Nq * 7 + Nk)
+
+
+@pytest.mark.parametrize("G", [1, 2, 8, 32])
+def test_bwd_gqa_groups(G):
+    check(1, G * 2, 2, 96, 96, 128, "bf16", True, seed=G)
+
+
+@pytest.mark.parametrize("which", ["zero", "neg", "big"])
+def test_bwd_scales(which):
+    sc = {"zero": 0.0, "neg": -0.3, "big": 0.5}[which]
+    check(1, 2, 2, 65, 65, 64, "f32", True, scale=sc, seed=3)
+    check(1, 2, 1, 65, 65, 64, "f16", False, scale=sc, seed=4)
+
+
+def test_bwd_training_shape_sampled():
+    """bf16 causal GQA at a training length (B1 Hq32 Hkv8 N2048 d128): every gradient row
+    of two query heads and their shared key/value head against the oracle, which needs only
+    those heads (a key/value head's gradient is the sum over its own query group)."""
+    B, Hq, Hkv, N, d = 1, 32, 8, 2048, 128
+    (q, k, v, do, sc), (o, lse, dq, dk, dv) = run(B, Hq, Hkv, N, N, d, "bf16", True, seed=77)
+    hk = 5
+    sl = slice(hk * 4, hk * 4 + 4)                     # the 4 query heads sharing kv head 5
+    rdq, rdk, rdv = oracle.attention_ref_bwd(q[:, sl], k[:, hk:hk + 1], v[:, hk:hk + 1],
+                                             do[:, sl], causal=True, scale=sc)
+    errs = {"dq": rel_err(dq[:, sl], rdq), "dk": rel_err(dk[:, hk:hk + 1], rdk),
+            "dv": rel_err(dv[:, hk:hk + 1], rdv)}
+    print("  errors", errs, flush=True)
+    for name, e in errs.items():
+        assert e <= GTOL["bf16"], f"{name} relative err {e}"
+    ref_lse = oracle.attention_ref_lse(q[:, sl], k[:, hk:hk + 1], v[:, hk:hk + 1], causal=True,
+                                       scale=sc)
+    assert float(np.max(np.abs(lse[:, sl] - ref_lse) / np.maximum(1, np.abs(ref_lse)))) <= \
+        LSE_TOL["bf16"]
+
+
+def test_bwd_no_queries_gives_zero_kv_gradients():
+    """seqlen_q = 0 against 50 keys (non-causal): dK and dV are written as zeros."""
+    k = torch.randn(1, 2, 50, 64, device="cuda", dtype=torch.bfloat16)
+    q = torch.empty(1, 4, 0, 64, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(1, 4, 0, device="cuda", dtype=torch.float32)
+    dq, dk, dv = aule.flash_attention_backward(q, k, k.clone(), q, q.clone(), lse, causal=False)
+    torch.cuda.synchronize()
+    assert dq.numel() == 0 and bool((dk == 0).all()) and bool((dv == 0).all())
+
+
+def test_bwd_non_default_stream():
+    q, k, v = dense_inputs(1, 2, 1, 70, 70, 64, seed=9, dtype="f16")
+    do = grad_out(q.shape, 9, "f16")
+    tq, tk, tv, tdo = dev(q, "f16"), dev(k, "f16"), dev(v, "f16"), dev(do, "f16")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        o, lse = aule.flash_attention(tq, tk, tv, causal=True, return_lse=True)
+        dq, dk, dv = aule.flash_attention_backward(tq, tk, tv, o, tdo, lse, causal=True)
+    s.synchronize()
+    rdq, rdk, rdv = oracle.attention_ref_bwd(q, k, v, do, causal=True, scale=1 / 8)
+    for got, ref in ((dq, rdq), (dk, rdk), (dv, rdv)):
+        assert rel_err(host(got), ref) <= GTOL["f16"]

@@ -16,6 +16,9 @@ wrappers follow the pages' APIs:
   [total_tokens, 3, heads, head_dim] with cumulative ``cu_seqlens``, ``causal`` defaulting
   to False (ewbang.com article on a PyTorch FlashAttention for Turing, signature and
   docstring of the varlen function; its unsupported options raise NotImplementedError);
+* ``flash_attention(..., return_lse=True)`` and ``flash_attention_backward(q, k, v, out, dout,
+  lse)`` — the per-row log-sum-exp and the gradients (dq, dk, dv), the score matrix
+  recomputed in the backward (FlashAttention-T commentary, FAQ 4, training bullet);
 * ``flash_attention_decode(q, k, v, causal=True, scale=None, num_splits=0)`` — a few new
   queries against a key/value cache, split over the key range (FlashAttention-T
   commentary, FAQ 4: the KV cache processed in blocks at inference); causal masking is
@@ -37,8 +40,9 @@ LIB_PATH = os.environ.get("AULE_LIB") or os.path.join(_PKG, "libaule_attn.so")
 AULE_DTYPE_F32, AULE_DTYPE_F16, AULE_DTYPE_BF16 = 0, 1, 2
 AULE_OK, AULE_ERR_INVALID_ARGUMENT, AULE_ERR_UNSUPPORTED, AULE_ERR_HIP = 0, 1, 2, 3
 
-EXPORTED = ("aule_attn_fwd", "aule_attn_fwd_varlen", "aule_attn_fwd_splitkv",
-            "aule_attn_splitkv_workspace_size", "aule_status_string", "aule_last_error")
+EXPORTED = ("aule_attn_fwd", "aule_attn_fwd_lse", "aule_attn_bwd", "aule_attn_fwd_varlen",
+            "aule_attn_fwd_splitkv", "aule_attn_splitkv_workspace_size", "aule_status_string",
+            "aule_last_error")
 
 _lib = None
 
@@ -66,6 +70,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.aule_attn_fwd_varlen.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                          ctypes.c_int, vp]
     lib.aule_attn_fwd_varlen.restype = ctypes.c_int
+    lib.aule_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
+                                      ctypes.c_int, vp]
+    lib.aule_attn_fwd_lse.restype = ctypes.c_int
+    lib.aule_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                  i32, f32, ctypes.c_int, vp]
+    lib.aule_attn_bwd.restype = ctypes.c_int
     lib.aule_attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                           ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
     lib.aule_attn_fwd_splitkv.restype = ctypes.c_int
@@ -87,6 +97,22 @@ def aule_attn_fwd(q, k, v, o, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head
     return load_library().aule_attn_fwd(q, k, v, o, batch, heads_q, heads_kv, seqlen_q,
                                         seqlen_k, head_dim, int(causal), float(scale),
                                         int(dtype), stream)
+
+
+def aule_attn_fwd_lse(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
+                      causal, scale, dtype, stream=0) -> int:
+    """Raw call: device pointers as ints; returns the status code."""
+    return load_library().aule_attn_fwd_lse(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q,
+                                            seqlen_k, head_dim, int(causal), float(scale),
+                                            int(dtype), stream)
+
+
+def aule_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, batch, heads_q, heads_kv, seqlen_q,
+                  seqlen_k, head_dim, causal, scale, dtype, stream=0) -> int:
+    """Raw call: device pointers as ints; returns the status code."""
+    return load_library().aule_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, batch, heads_q,
+                                        heads_kv, seqlen_q, seqlen_k, head_dim, int(causal),
+                                        float(scale), int(dtype), stream)
 
 
 def aule_attn_fwd_varlen(qkv, cu_seqlens, o, num_seqs, total_tokens, max_seqlen, heads,
@@ -155,8 +181,11 @@ def _need_gpu_tensor(name, t):
         raise ValueError(f"{name} must be contiguous")
 
 
-def flash_attention(q, k, v, causal: bool = True, scale: float | None = None, out=None):
-    """O = softmax(scale * q k^T [+ causal mask]) v for q [B,Hq,N,d], k/v [B,Hkv,Nk,d]."""
+def flash_attention(q, k, v, causal: bool = True, scale: float | None = None, out=None,
+                    return_lse: bool = False):
+    """O = softmax(scale * q k^T [+ causal mask]) v for q [B,Hq,N,d], k/v [B,Hkv,Nk,d].
+    With ``return_lse`` also returns the fp32 per-row log-sum-exp [B,Hq,N] the backward
+    needs: (out, lse)."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need_gpu_tensor(name, t)
@@ -176,11 +205,45 @@ def flash_attention(q, k, v, causal: bool = True, scale: float | None = None, ou
         _need_gpu_tensor("out", out)
         if out.shape != q.shape or out.dtype != q.dtype:
             raise ValueError("out must match q in shape and dtype")
+    if return_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+        st = aule_attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, causal, scale,
+                               dtype_code(q.dtype), _stream_handle(q.device))
+        _check(st)
+        return out, lse
     st = aule_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv,
                        Nq, Nk, d, causal, scale, dtype_code(q.dtype),
                        _stream_handle(q.device))
     _check(st)
     return out
+
+
+def flash_attention_backward(q, k, v, out, dout, lse, causal: bool = True,
+                             scale: float | None = None):
+    """Gradients (dq, dk, dv) of flash_attention(q, k, v, causal, scale) = out for the output
+    gradient dout, from the lse that flash_attention(..., return_lse=True) returned."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse)):
+        _need_gpu_tensor(name, t)
+    if not (q.dtype == k.dtype == v.dtype == out.dtype == dout.dtype):
+        raise TypeError("q, k, v, out and dout must share a dtype")
+    if q.dim() != 4 or k.dim() != 4 or tuple(k.shape) != tuple(v.shape):
+        raise ValueError("q [B,Hq,N,d], k and v [B,Hkv,Nk,d]")
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    if out.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("out and dout must have the shape of q")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("lse must be float32 [B, Hq, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = aule_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                       lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq,
+                       Nk, d, causal, scale, dtype_code(q.dtype), _stream_handle(q.device))
+    _check(st)
+    return dq, dk, dv
 
 
 def flash_attention_decode(q, k, v, causal: bool = True, scale: float | None = None,
@@ -272,7 +335,8 @@ def flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen, dropout_p=0.0,
     return out
 
 
-__all__ = ["aule_attn_fwd", "aule_attn_fwd_varlen", "aule_attn_fwd_splitkv",
+__all__ = ["aule_attn_fwd", "aule_attn_fwd_lse", "aule_attn_bwd", "aule_attn_fwd_varlen",
+           "aule_attn_fwd_splitkv", "flash_attention_backward",
            "aule_attn_splitkv_workspace_size", "aule_status_string", "aule_last_error",
            "flash_attention", "flash_attention_decode", "flash_attn_varlen_qkvpacked_func",
            "load_library", "AuleError", "LIB_PATH", "EXPORTED"]

@@ -403,8 +403,7 @@ __global__ __launch_bounds__(64) void attn_decode_combine_kernel(DecodeProblem p
             l = fmaf(p.ws_ml[2 * slot + 1], w, l);
         }
         const int n = min(64, S - s0);
-#pragma unroll 8
-        for (int j = 0; j < n; ++j) {
+        for (int j = 0; j < n; ++j) {   // independent loads: issued back to back
             const float wj = __shfl(w, j);
             const int64_t slot = (int64_t)(s0 + j) * rows_total + row;
 #pragma unroll

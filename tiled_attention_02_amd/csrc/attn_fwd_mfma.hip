@@ -271,6 +271,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         int Lq, Lk, qr0, nsub, n_kt;   // lengths, first row of this wave, sub-steps, K/V tiles
         const T* qb;                   // this wave's Q slice and O slice
         T* ob;
+        float* lseb;                   // this wave's log-sum-exp row (dense, optional)
         i32x4 rk, rv;                  // K / V slice descriptors, exactly the Lk valid rows
     };
     const int ngroups = p.heads_q / GH;
@@ -311,6 +312,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         it.qr0 = tile * BMW + kRowsPerWave * (wave / GH);
         it.qb = static_cast<const T*>(p.q) + (VARLEN ? tok0 * p.q_rstride : bidx * p.q_bstride) + hq * p.q_hstride;
         it.ob = static_cast<T*>(p.o) + (VARLEN ? tok0 * p.o_rstride : bidx * p.o_bstride) + hq * p.o_hstride;
+        it.lseb = (!VARLEN && p.lse) ? p.lse + ((int64_t)bidx * p.heads_q + hq) * p.seqlen_q : nullptr;
         const T* kb = static_cast<const T*>(p.k) + (VARLEN ? tok0 * p.k_rstride : bidx * p.k_bstride) + hk * p.k_hstride;
         const T* vb = static_cast<const T*>(p.v) + (VARLEN ? tok0 * p.v_rstride : bidx * p.v_bstride) + hk * p.v_hstride;
         const int k_valid = Lk > 0 ? (int)((int64_t)(Lk - 1) * k_rs + hd * sizeof(T)) : 0;
@@ -553,10 +555,14 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     auto store_o = [&]() {
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
             cur.ob, (short)0, cur.Lq > 0 ? (int)((int64_t)cur.Lq * o_rs) : 0, (int)kBufferFlags);
+        float lse_row[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const float l = l_part[nb] + __shfl_xor(l_part[nb], 32);
             const float inv = 1.f / l;
+            // natural log-sum-exp of the scaled scores: t = scale * log2(e) * q.k, so
+            // log(sum exp(scale q.k)) = (m + log2 l) * ln 2
+            lse_row[nb] = (m_ref[nb] + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
             const uint32_t rowoff = (uint32_t)(cur.qr0 + 32 * nb + ln) * o_rs;
 #pragma unroll
             for (int db = 0; db < DB; ++db)
@@ -568,6 +574,15 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                     const uint32_t off = d0 < hd ? rowoff + (uint32_t)d0 * (uint32_t)sizeof(T) : kOobOffset;
                     __builtin_amdgcn_raw_buffer_store_b64(w, ro, (int)off, 0, 0);
                 }
+        }
+        // after the O stores: the persistent form's wait for the next item only needs every
+        // store to be newer than that item's loads
+        if (cur.lseb) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = cur.qr0 + 32 * nb + ln;
+                if (h == 0 && row < cur.Lq) cur.lseb[row] = lse_row[nb];
+            }
         }
     };
 

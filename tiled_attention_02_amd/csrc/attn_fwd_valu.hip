@@ -131,6 +131,8 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_valu_kernel(AttnProblem p) 
         }
     }
 
+    if (!VARLEN && p.lse && c == 0 && i < Lq)   // natural log-sum-exp of the scaled scores
+        p.lse[((int64_t)slot.seq * p.heads_q + hq) * p.seqlen_q + i] = (m + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
     if (i < Lq) {
         float inv = 1.f / l;
 #pragma unroll

@@ -37,6 +37,7 @@ struct AttnProblem {
     const int32_t* cu_seqlens;  // varlen only, else nullptr
     int32_t total_tokens;       // varlen only
     int32_t max_seqlen;         // varlen hint
+    float* lse;                 // dense only, optional: per-row log-sum-exp [batch, heads_q, seqlen_q]
 };
 
 // Launchers. Each returns hipSuccess or the launch error; none synchronises.

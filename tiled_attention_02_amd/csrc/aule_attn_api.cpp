@@ -11,6 +11,7 @@
 #include <cstdlib>
 
 #include "aule_attn.h"
+#include "attn_bwd.h"
 #include "attn_decode.h"
 #include "attn_problem.h"
 
@@ -129,13 +130,14 @@ SplitPlan plan_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t 
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-aule_status_t aule_attn_fwd(const void* q, const void* k, const void* v, void* o,
-                            int32_t batch, int32_t heads_q, int32_t heads_kv,
-                            int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
-                            int32_t causal, float scale, aule_dtype_t dtype,
-                            hipStream_t stream) {
+// The dense checks shared by the forward entry points and the backward.
+aule_status_t check_dense(const void* q, const void* k, const void* v, const void* o,
+                          int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_q,
+                          int32_t seqlen_k, int32_t head_dim, int32_t causal, float scale,
+                          aule_dtype_t dtype, bool* empty) {
+    *empty = false;
     if (batch < 0 || seqlen_q < 0)
         return fail(AULE_ERR_INVALID_ARGUMENT, "batch and seqlen_q must be >= 0");
     if (aule_status_t st = check_common(head_dim, scale, dtype)) return st;
@@ -146,8 +148,8 @@ aule_status_t aule_attn_fwd(const void* q, const void* k, const void* v, void* o
     if (causal && seqlen_q != seqlen_k)
         return fail(AULE_ERR_UNSUPPORTED, "causal attention needs seqlen_q == seqlen_k (got %d, %d)", seqlen_q, seqlen_k);
     if (batch == 0 || seqlen_q == 0) {
-        g_last_error[0] = '\0';
-        return AULE_OK;  // empty problem
+        *empty = true;
+        return AULE_OK;
     }
     if (seqlen_k <= 0)
         return fail(AULE_ERR_INVALID_ARGUMENT, "seqlen_k must be positive for a non-empty problem");
@@ -155,11 +157,34 @@ aule_status_t aule_attn_fwd(const void* q, const void* k, const void* v, void* o
         return fail(AULE_ERR_INVALID_ARGUMENT, "null tensor pointer");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
         return fail(AULE_ERR_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+    return AULE_OK;
+}
+
+aule_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_q,
+                       int32_t seqlen_k, int32_t head_dim, int32_t causal, float scale,
+                       aule_dtype_t dtype, hipStream_t stream) {
+    bool empty;
+    if (aule_status_t st = check_dense(q, k, v, o, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
+                                       head_dim, causal, scale, dtype, &empty))
+        return st;
+    if (empty) {
+        g_last_error[0] = '\0';
+        return AULE_OK;  // empty problem
+    }
     const size_t es = elem_size(dtype);
     const size_t nq = (size_t)batch * heads_q * seqlen_q * head_dim * es;
     const size_t nkv = (size_t)batch * heads_kv * seqlen_k * head_dim * es;
     if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
         return fail(AULE_ERR_INVALID_ARGUMENT, "output overlaps an input");
+    if (lse) {
+        const size_t nl = (size_t)batch * heads_q * seqlen_q * sizeof(float);
+        if (reinterpret_cast<uintptr_t>(lse) & 3u)
+            return fail(AULE_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+        if (overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nkv) || overlaps(lse, nl, v, nkv) ||
+            overlaps(lse, nl, o, nq))
+            return fail(AULE_ERR_INVALID_ARGUMENT, "lse overlaps a tensor");
+    }
 
     aule::AttnProblem p{};
     p.q = q; p.k = k; p.v = v; p.o = o;
@@ -174,7 +199,106 @@ aule_status_t aule_attn_fwd(const void* q, const void* k, const void* v, void* o
     p.cu_seqlens = nullptr;
     p.total_tokens = 0;
     p.max_seqlen = seqlen_q;
+    p.lse = lse;
     return dispatch(p, dtype, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+aule_status_t aule_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv,
+                            int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                            int32_t causal, float scale, aule_dtype_t dtype,
+                            hipStream_t stream) {
+    return fwd_impl(q, k, v, o, nullptr, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
+                    causal, scale, dtype, stream);
+}
+
+aule_status_t aule_attn_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                                int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                int32_t causal, float scale, aule_dtype_t dtype,
+                                hipStream_t stream) {
+    if (!lse && batch > 0 && seqlen_q > 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "null lse pointer");
+    return fwd_impl(q, k, v, o, lse, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
+                    causal, scale, dtype, stream);
+}
+
+aule_status_t aule_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                            const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                            int32_t batch, int32_t heads_q, int32_t heads_kv,
+                            int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                            int32_t causal, float scale, aule_dtype_t dtype,
+                            hipStream_t stream) {
+    bool empty;
+    if (aule_status_t st = check_dense(q, k, v, o, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
+                                       head_dim, causal, scale, dtype, &empty))
+        return st;
+    // With no query rows but keys present, dK and dV are all zero and still written.
+    const bool zero_kv_only = empty && batch > 0 && seqlen_q == 0 && seqlen_k > 0;
+    if (empty && !zero_kv_only) {
+        g_last_error[0] = '\0';
+        return AULE_OK;
+    }
+    if (zero_kv_only) {
+        if (!dk || !dv)
+            return fail(AULE_ERR_INVALID_ARGUMENT, "null pointer");
+        if (!aligned16(dk) || !aligned16(dv))
+            return fail(AULE_ERR_INVALID_ARGUMENT, "misaligned pointer");
+        const size_t nkv = (size_t)batch * heads_kv * seqlen_k * head_dim * elem_size(dtype);
+        if (overlaps(dk, nkv, dv, nkv))
+            return fail(AULE_ERR_INVALID_ARGUMENT, "gradient buffers overlap");
+        if (batch > 65535)
+            return fail(AULE_ERR_UNSUPPORTED, "batch must be at most 65535 for the backward");
+        aule::BwdProblem p{};
+        p.dk = dk; p.dv = dv;
+        p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
+        p.seqlen_q = 0; p.seqlen_k = seqlen_k; p.head_dim = head_dim;
+        p.scale = scale;
+        const hipError_t err = aule::launch_attn_bwd(p, static_cast<aule::Dtype>(dtype), stream);
+        if (err != hipSuccess)
+            return fail(AULE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+        g_last_error[0] = '\0';
+        return AULE_OK;
+    }
+    if (!dout || !lse || !dq || !dk || !dv)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv) ||
+        (reinterpret_cast<uintptr_t>(lse) & 3u))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "misaligned pointer");
+    if (batch > 65535 || heads_q > 65535)   // grid z and y dimensions
+        return fail(AULE_ERR_UNSUPPORTED, "batch and heads_q must be at most 65535 for the backward");
+    const size_t es = elem_size(dtype);
+    const size_t nq = (size_t)batch * heads_q * seqlen_q * head_dim * es;
+    const size_t nkv = (size_t)batch * heads_kv * seqlen_k * head_dim * es;
+    const size_t nl = (size_t)batch * heads_q * seqlen_q * sizeof(float);
+    const void* ins[] = {q, k, v, o, dout, lse};
+    const size_t nin[] = {nq, nkv, nkv, nq, nq, nl};
+    void* outs[] = {dq, dk, dv};
+    const size_t nout[] = {nq, nkv, nkv};
+    for (int a = 0; a < 3; ++a) {
+        for (int b2 = 0; b2 < 6; ++b2)
+            if (overlaps(outs[a], nout[a], ins[b2], nin[b2]))
+                return fail(AULE_ERR_INVALID_ARGUMENT, "a gradient buffer overlaps an input");
+        for (int b2 = a + 1; b2 < 3; ++b2)
+            if (overlaps(outs[a], nout[a], outs[b2], nout[b2]))
+                return fail(AULE_ERR_INVALID_ARGUMENT, "gradient buffers overlap");
+    }
+    aule::BwdProblem p{};
+    p.q = q; p.k = k; p.v = v; p.o = o; p.do_ = dout; p.lse = lse;
+    p.dq = dq; p.dk = dk; p.dv = dv;
+    p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
+    p.seqlen_q = seqlen_q; p.seqlen_k = seqlen_k; p.head_dim = head_dim;
+    p.causal = causal ? 1 : 0;
+    p.scale = scale;
+    const hipError_t err = aule::launch_attn_bwd(p, static_cast<aule::Dtype>(dtype), stream);
+    if (err != hipSuccess)
+        return fail(AULE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
+    g_last_error[0] = '\0';
+    return AULE_OK;
 }
 
 aule_status_t aule_attn_fwd_varlen(const void* qkv, const int32_t* cu_seqlens, void* o,
