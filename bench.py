@@ -11,6 +11,9 @@ against the MI355X dense bf16 MFMA peak; `cpu_baseline` times the CPU fp64 oracl
 bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+Other workloads (--workload): the dense, varlen and long-context forward cases, the split-KV
+decode case (GB/s against the HBM roofline) and the backward of the headline shape.
 """
 import argparse
 import json
@@ -34,6 +37,10 @@ DECODE_SOURCES = ["tiled_attention_02_amd/csrc/attn_decode.hip",
                   "tiled_attention_02_amd/csrc/attn_decode.h",
                   "tiled_attention_02_amd/csrc/attn_device.h",
                   "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
+BWD_SOURCES = ["tiled_attention_02_amd/csrc/attn_bwd.hip",
+               "tiled_attention_02_amd/csrc/attn_bwd.h",
+               "tiled_attention_02_amd/csrc/attn_device.h",
+               "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -47,7 +54,12 @@ def kernel_source_hash(sources=KERNEL_SOURCES):
 
 
 def sources_for(workload):
-    return DECODE_SOURCES if workload.startswith("d") else KERNEL_SOURCES
+    from workloads import BWD_CONFIGS, DECODE_CONFIGS
+    if workload in DECODE_CONFIGS:
+        return DECODE_SOURCES
+    if workload in BWD_CONFIGS:
+        return BWD_SOURCES
+    return KERNEL_SOURCES
 
 
 def measured_traffic(workload):
@@ -90,8 +102,13 @@ def parse():
 
 
 def device_inputs(cfg, torch):
-    from workloads import DecodeConfig, DenseConfig
+    from workloads import BwdConfig, DecodeConfig, DenseConfig
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
+    if isinstance(cfg, BwdConfig):
+        q, k, v = cfg.inputs()
+        do = cfg.grad()
+        t = lambda x: torch.from_numpy(x).to(device="cuda", dtype=tdt)
+        return (t(q), t(k), t(v), t(do)), (q, k, v, do)
     if isinstance(cfg, (DenseConfig, DecodeConfig)):
         q, k, v = cfg.inputs()
         t = lambda x: torch.from_numpy(x).to(device="cuda", dtype=tdt)
@@ -103,7 +120,16 @@ def device_inputs(cfg, torch):
 
 def make_step(cfg, dev_inputs, torch):
     import tiled_attention_02_amd as aule
-    from workloads import DecodeConfig, DenseConfig
+    from workloads import BwdConfig, DecodeConfig, DenseConfig
+    if isinstance(cfg, BwdConfig):
+        # O and the row LSE come from one forward before the timed region; a step is the
+        # backward alone (both of its kernels)
+        q, k, v, do = dev_inputs
+        o, lse = aule.flash_attention(q, k, v, causal=cfg.causal, scale=cfg.softmax_scale,
+                                      return_lse=True)
+        grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+        return lambda: aule.flash_attention_backward(q, k, v, o, do, lse, causal=cfg.causal,
+                                                     scale=cfg.softmax_scale, grads=grads)
     if isinstance(cfg, DecodeConfig):
         q, k, v = dev_inputs
         out = torch.empty_like(q)
@@ -149,8 +175,34 @@ def cpu_baseline(cfg, host_inputs, budget_s):
     fit in about budget_s seconds; scaled to TFLOP/s with the same FLOP count."""
     import numpy as np
     import oracle
-    from workloads import DecodeConfig, DenseConfig
+    from workloads import BwdConfig, DecodeConfig, DenseConfig
     threads = len(os.sched_getaffinity(0))
+    if isinstance(cfg, BwdConfig):
+        # whole (batch, query head) slices: the oracle's gradients of one query head against
+        # its kv head, 10*d FLOP per unmasked pair like the GPU figure
+        q, k, v, do = host_inputs
+        G = cfg.heads_q // cfg.heads_kv
+        n = cfg.seqlen
+        pairs = n * (n + 1) // 2 if cfg.causal else n * n
+        t0 = time.perf_counter()
+        heads = 0
+        for b in range(cfg.batch):
+            for hq in range(cfg.heads_q):
+                hk = hq // G
+                oracle.attention_ref_bwd(q[b:b + 1, hq:hq + 1], k[b:b + 1, hk:hk + 1],
+                                         v[b:b + 1, hk:hk + 1], do[b:b + 1, hq:hq + 1],
+                                         causal=cfg.causal, scale=cfg.softmax_scale)
+                heads += 1
+                if time.perf_counter() - t0 > budget_s:
+                    break
+            else:
+                continue
+            break
+        dt = time.perf_counter() - t0
+        return {"value": 10 * cfg.head_dim * pairs * heads / dt / 1e12, "unit": "TFLOP/s",
+                "cores": threads, "kind": "oracle",
+                "sample": f"{heads} of {cfg.batch * cfg.heads_q} (batch, query head) slices in "
+                f"full, {dt:.1f} s"}
     if isinstance(cfg, DecodeConfig):
         # whole (batch, query head) slices against their kv head's cache; scaled to GB/s of
         # the workload's compulsory bytes like the GPU figure
@@ -225,8 +277,8 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
-    from workloads import CONFIGS, DECODE_CONFIGS, DecodeConfig
-    ALL = {**CONFIGS, **DECODE_CONFIGS}
+    from workloads import BWD_CONFIGS, CONFIGS, DECODE_CONFIGS, BwdConfig, DecodeConfig
+    ALL = {**CONFIGS, **DECODE_CONFIGS, **BWD_CONFIGS}
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
@@ -268,6 +320,8 @@ def main():
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": cfg.bytes_compulsory()},
     }
+    if isinstance(cfg, BwdConfig):
+        line["metric"] = "attention bwd TFLOPS (causal-adjusted, 2.5x forward FLOPs) and % of MI355X bf16 MFMA peak"
     if isinstance(cfg, DecodeConfig):
         # reading the KV cache bounds this path: throughput against the HBM roofline
         gbs = cfg.bytes_compulsory() / kern_s / 1e9
@@ -296,7 +350,11 @@ def main():
 
 
 def describe(cfg):
-    from workloads import DecodeConfig, DenseConfig
+    from workloads import BwdConfig, DecodeConfig, DenseConfig
+    if isinstance(cfg, BwdConfig):
+        return (f"{cfg.dtype} backward {'causal' if cfg.causal else 'non-causal'} B={cfg.batch} "
+                f"Hq={cfg.heads_q} Hkv={cfg.heads_kv} N={cfg.seqlen} d={cfg.head_dim} "
+                f"scale={cfg.softmax_scale:.6g}")
     if isinstance(cfg, DecodeConfig):
         return (f"{cfg.dtype} decode {'causal' if cfg.causal else 'non-causal'} B={cfg.batch} "
                 f"Hq={cfg.heads_q} Hkv={cfg.heads_kv} Nq={cfg.seqlen_q} Nk={cfg.seqlen_k} "

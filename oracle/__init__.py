@@ -6,7 +6,8 @@ may import or run it. It shares no code with the HIP library.
 """
 from .attention import (attention_ref, attention_ref_bwd, attention_ref_decode,
                         attention_ref_lse, attention_ref_rows, attention_ref_varlen,
-                        attention_ref_varlen_rows)
+                        attention_ref_varlen_mods, attention_ref_varlen_rows)
 
 __all__ = ["attention_ref", "attention_ref_bwd", "attention_ref_decode", "attention_ref_lse",
-           "attention_ref_rows", "attention_ref_varlen", "attention_ref_varlen_rows"]
+           "attention_ref_rows", "attention_ref_varlen", "attention_ref_varlen_mods",
+           "attention_ref_varlen_rows"]

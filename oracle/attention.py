@@ -40,6 +40,15 @@ Readings where the pages are silent:
     Nk cached keys; under causal masking the new queries are the last Nq positions of the
     sequence (bottom-right alignment: query i sees keys j <= i + Nk - Nq), so decoding them
     reproduces the last Nq rows of causal attention over the whole sequence;
+  * the score modifiers of the varlen signature (window_size, softcap, alibi_slopes), which
+    the ewbang.com varlen docstring names as parameters (sliding window (left, right), -1 for
+    unbounded; a soft-capping value; ALiBi slopes of shape [heads] or [batch, heads]) without
+    defining them, take their usual reading: with x = scale * q_i . k_j,
+        x <- softcap * tanh(x / softcap)          if softcap > 0
+        x <- x - slope[s, h] * |i - j|            if slopes are given (s = sequence, h = head)
+    and key j is visible to query i iff it is inside the sequence, j <= i when causal,
+    j >= i - left when left >= 0 and j <= i + right when right >= 0 (positions counted from
+    the sequence start; causal with right = -1 or 0 is the same mask);
   * the scale is applied to the float64 dot product as the exact float32 value the
     library receives;
   * inputs are the values already rounded to the storage dtype (the generators do that);
@@ -189,6 +198,83 @@ def attention_ref_varlen_rows(qkv, cu_seqlens, tokens, *, causal: bool,
         q, k, v = _seq_as_dense(qkv, a, e)
         res = attention_ref_rows(q, k, v, local, causal=causal, scale=scale)[0]
         out[sel] = res.transpose(1, 0, 2)
+    return out
+
+
+def _window_masked(rows, n_keys: int, left: int, right: int) -> np.ndarray:
+    """Boolean [len(rows), n_keys]: True where key j lies outside the sliding window of
+    query row i (before i - left when left >= 0, after i + right when right >= 0)."""
+    rows = np.asarray(rows)[:, None]
+    j = np.arange(n_keys)[None, :]
+    out = np.zeros((rows.shape[0], n_keys), dtype=bool)
+    if left >= 0:
+        out |= j < rows - left
+    if right >= 0:
+        out |= j > rows + right
+    return out
+
+
+def _softcap(S: np.ndarray, cap: float) -> np.ndarray:
+    """Soft capping of scaled scores: cap * tanh(S / cap), odd, slope 1 at 0, |.| < cap."""
+    return cap * np.tanh(S / cap)
+
+
+def _alibi_bias(rows, n_keys: int, slope: float) -> np.ndarray:
+    """ALiBi: a penalty growing linearly with the distance between query i and key j."""
+    return -slope * np.abs(np.asarray(rows)[:, None] - np.arange(n_keys)[None, :]).astype(np.float64)
+
+
+def _check_mods(window, softcap, alibi_slopes, n_seqs, heads):
+    left, right = (int(window[0]), int(window[1]))
+    if left < -1 or right < -1:
+        raise ValueError("window sizes must be >= -1")
+    cap = float(np.float32(softcap))
+    if not np.isfinite(cap) or cap < 0:
+        raise ValueError("softcap must be finite and >= 0")
+    slopes = None
+    if alibi_slopes is not None:
+        a = np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64)
+        if a.shape == (heads,):
+            slopes = np.broadcast_to(a, (n_seqs, heads))
+        elif a.shape == (n_seqs, heads):
+            slopes = a
+        else:
+            raise ValueError("alibi_slopes must be [heads] or [batch, heads]")
+    return left, right, cap, slopes
+
+
+def attention_ref_varlen_mods(qkv, cu_seqlens, *, causal: bool, scale: float,
+                              window=(-1, -1), softcap: float = 0.0, alibi_slopes=None,
+                              tokens=None) -> np.ndarray:
+    """Varlen attention with the score modifiers (sliding window, soft cap, ALiBi) in the
+    order: scaled dot product, soft cap, ALiBi bias, masks (causal, window), softmax, times V.
+    ``tokens`` limits the result to those global token indices (in the order given);
+    otherwise every token. Returns float64 [T or len(tokens), H, d]."""
+    qkv, cu = _check_varlen(qkv, cu_seqlens)
+    T, _, H, d = qkv.shape
+    left, right, cap, slopes = _check_mods(window, softcap, alibi_slopes, cu.size - 1, H)
+    sc = _scale64(scale)
+    tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    if tok.size and (tok.min() < 0 or tok.max() >= T):
+        raise ValueError("token index out of range")
+    out = np.empty((tok.size, H, d), dtype=np.float64)
+    seq_of = np.searchsorted(cu, tok, side="right") - 1
+    for s in np.unique(seq_of):
+        a, e = int(cu[s]), int(cu[s + 1])
+        sel = np.nonzero(seq_of == s)[0]
+        rows = tok[sel] - a
+        L = e - a
+        masked = _window_masked(rows, L, left, right)
+        if causal:
+            masked |= _causal_masked(rows, L)
+        for h in range(H):
+            S = sc * (qkv[a + rows, 0, h] @ qkv[a:e, 1, h].T)
+            if cap > 0:
+                S = _softcap(S, cap)
+            if slopes is not None:
+                S = S + _alibi_bias(rows, L, slopes[s, h])
+            S[masked] = -np.inf
+            out[sel, h] = _softmax_rows_times_v(S, qkv[a:e, 2, h])
     return out
 
 

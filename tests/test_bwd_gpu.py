@@ -21,7 +21,7 @@ import pytest
 
 import oracle
 import tiled_attention_02_amd as aule
-from workloads import dense_inputs, round_to_dtype
+from workloads import BWD_CONFIGS, dense_inputs, output_grad
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -46,11 +46,6 @@ def host(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def grad_out(shape, seed, dtype):
-    rng = np.random.default_rng(seed + 1000)
-    return round_to_dtype(rng.standard_normal(shape, dtype=np.float32), dtype)
-
-
 def rel_err(got, ref):
     return float(np.max(np.abs(got - ref))) / max(1.0, float(np.max(np.abs(ref))))
 
@@ -59,7 +54,7 @@ def run(B, Hq, Hkv, Nq, Nk, d, dtype, causal, scale=None, seed=0):
     print(f"bwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal} "
           f"scale={scale} seed={seed}", flush=True)
     q, k, v = dense_inputs(B, Hq, Hkv, Nq, Nk, d, seed=seed, dtype=dtype)
-    do = grad_out(q.shape, seed, dtype)
+    do = output_grad(q.shape, seed=seed, dtype=dtype)
     sc = 1.0 / math.sqrt(d) if scale is None else scale
     tq, tk, tv, tdo = dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(do, dtype)
     o, lse = aule.flash_attention(tq, tk, tv, causal=causal, scale=sc, return_lse=True)
@@ -147,7 +142,7 @@ def test_bwd_no_queries_gives_zero_kv_gradients():
 
 def test_bwd_non_default_stream():
     q, k, v = dense_inputs(1, 2, 1, 70, 70, 64, seed=9, dtype="f16")
-    do = grad_out(q.shape, 9, "f16")
+    do = output_grad(q.shape, seed=9, dtype="f16")
     tq, tk, tv, tdo = dev(q, "f16"), dev(k, "f16"), dev(v, "f16"), dev(do, "f16")
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())

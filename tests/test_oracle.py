@@ -573,6 +573,178 @@ def test_backward_single_key():
     np.testing.assert_allclose(dv[0, 1, 0], do[0, 2:4].sum(axis=(0, 1)), atol=1e-13)
 
 
+# ---------------------------------------------------------------- score modifiers
+
+def _mods_inputs(lengths, H, d, seed):
+    rng = np.random.default_rng(seed)
+    cu = cu_seqlens_from_lengths(lengths)
+    return rng.standard_normal((int(cu[-1]), 3, H, d)), cu
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_mods_defaults_are_plain_varlen(causal):
+    qkv, cu = _mods_inputs([5, 9, 1, 0, 4], 2, 4, 501)
+    got = oracle.attention_ref_varlen_mods(qkv, cu, causal=causal, scale=0.5)
+    ref = oracle.attention_ref_varlen(qkv, cu, causal=causal, scale=0.5)
+    np.testing.assert_allclose(got, ref, atol=1e-13)
+
+
+def test_window_unbounded_left_zero_right_is_causal():
+    qkv, cu = _mods_inputs([7, 3, 12], 3, 5, 502)
+    got = oracle.attention_ref_varlen_mods(qkv, cu, causal=False, scale=0.3, window=(-1, 0))
+    ref = oracle.attention_ref_varlen(qkv, cu, causal=True, scale=0.3)
+    np.testing.assert_allclose(got, ref, atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_zero_returns_own_value(causal):
+    """A (0, 0) window leaves each query only its own key: O = V row for row, exactly."""
+    qkv, cu = _mods_inputs([6, 1, 9], 2, 3, 503)
+    got = oracle.attention_ref_varlen_mods(qkv, cu, causal=causal, scale=0.7, window=(0, 0),
+                                           softcap=2.0, alibi_slopes=[0.5, 0.25])
+    np.testing.assert_array_equal(got, qkv[:, 2])
+
+
+@pytest.mark.parametrize("window", [(3, 1), (0, 4), (2, -1), (-1, 2)])
+def test_window_identical_keys_mean(window):
+    """Equal keys give equal scores, so each query averages V over its window: keys
+    max(0, i - left) .. min(L - 1, i + right); with V = identity that is a box row."""
+    L = 10
+    qkv = np.zeros((L, 3, 1, L))
+    qkv[:, 0, 0] = np.random.default_rng(511).standard_normal((L, L))
+    qkv[:, 1, 0] = np.random.default_rng(512).standard_normal(L)[None, :]
+    qkv[:, 2, 0] = np.eye(L)
+    cu = np.array([0, L], dtype=np.int32)
+    got = oracle.attention_ref_varlen_mods(qkv, cu, causal=False, scale=0.9, window=window)
+    left, right = window
+    ref = np.zeros((L, L))
+    for i in range(L):
+        lo = 0 if left < 0 else max(0, i - left)
+        hi = L - 1 if right < 0 else min(L - 1, i + right)
+        ref[i, lo:hi + 1] = 1.0 / (hi - lo + 1)
+    np.testing.assert_allclose(got[:, 0], ref, atol=1e-13)
+
+
+def _brute_mods(qkv, cu, causal, scale, window, softcap, slopes):
+    """Element by element in plain Python (math.exp / math.tanh), straight from the reading
+    of the modifiers."""
+    T, _, H, d = qkv.shape
+    left, right = window
+    sl = None if slopes is None else np.asarray(slopes, dtype=np.float32).reshape(-1, H)
+    out = np.zeros((T, H, d))
+    for s in range(len(cu) - 1):
+        a, e = int(cu[s]), int(cu[s + 1])
+        for h in range(H):
+            slope = 0.0 if sl is None else float(sl[s if sl.shape[0] > 1 else 0, h])
+            for i in range(e - a):
+                xs, vs = [], []
+                for j in range(e - a):
+                    if causal and j > i:
+                        continue
+                    if left >= 0 and j < i - left:
+                        continue
+                    if right >= 0 and j > i + right:
+                        continue
+                    x = scale * sum(qkv[a + i, 0, h, c] * qkv[a + j, 1, h, c] for c in range(d))
+                    if softcap > 0:
+                        x = softcap * math.tanh(x / softcap)
+                    x -= slope * abs(i - j)
+                    xs.append(x)
+                    vs.append(qkv[a + j, 2, h])
+                mx = max(xs)
+                ws = [math.exp(x - mx) for x in xs]
+                out[a + i, h] = sum(w * v for w, v in zip(ws, vs)) / sum(ws)
+    return out
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_mods_brute_force_tiny(seed):
+    rng = np.random.default_rng(600 + seed)
+    lengths = list(rng.integers(0, 8, size=3))
+    H, d = 2, 3
+    qkv, cu = _mods_inputs(lengths, H, d, 610 + seed)
+    qkv *= 2.0
+    causal = bool(seed % 2)
+    window = (int(rng.integers(-1, 4)), int(rng.integers(-1, 4)))
+    if causal and window[1] > 0:
+        window = (window[0], 0)
+    softcap = [0.0, 1.5, 4.0][seed % 3]
+    slopes = None if seed % 3 == 1 else (rng.uniform(0, 1, size=(3, H)).astype(np.float32)
+                                         if seed % 2 else rng.uniform(0, 1, size=H).astype(np.float32))
+    scale = 0.6
+    got = oracle.attention_ref_varlen_mods(qkv, cu, causal=causal, scale=scale, window=window,
+                                           softcap=softcap, alibi_slopes=slopes)
+    ref = _brute_mods(qkv, cu, causal, float(np.float32(scale)), window, softcap, slopes)
+    np.testing.assert_allclose(got, ref, atol=1e-12)
+
+
+def test_causal_alibi_is_a_key_bias():
+    """Under causal masking -slope * (i - j) = slope * j - slope * i, and a per-row constant
+    leaves the softmax unchanged: ALiBi equals plain causal attention with one extra
+    dimension carrying q = 1, k = slope * j / scale."""
+    L, H, d, scale = 11, 2, 4, 0.5
+    qkv, cu = _mods_inputs([L], H, d, 504)
+    slopes = np.array([0.375, 1.25], dtype=np.float32)
+    got = oracle.attention_ref_varlen_mods(qkv, cu, causal=True, scale=scale, alibi_slopes=slopes)
+    q = np.concatenate([qkv[:, 0], np.ones((L, H, 1))], axis=2).transpose(1, 0, 2)[None]
+    j = np.arange(L, dtype=np.float64)[:, None, None]
+    kx = (j * slopes.astype(np.float64)[None, :, None]) / scale
+    k = np.concatenate([qkv[:, 1], np.broadcast_to(kx, (L, H, 1))], axis=2).transpose(1, 0, 2)[None]
+    v = np.concatenate([qkv[:, 2], np.zeros((L, H, 1))], axis=2).transpose(1, 0, 2)[None]
+    ref = oracle.attention_ref(q, k, v, causal=True, scale=scale)[0].transpose(1, 0, 2)
+    np.testing.assert_allclose(got, ref[..., :d], atol=1e-12)
+
+
+def test_alibi_identical_keys_closed_form():
+    """Equal keys give equal scores, so non-causal ALiBi weights are exp(-slope |i - j|)
+    normalised; with V = identity, O[i] is that weight row."""
+    L, slope = 9, 0.8
+    qkv = np.zeros((L, 3, 1, L))
+    qkv[:, 0, 0] = np.random.default_rng(505).standard_normal((L, L))
+    qkv[:, 1, 0] = np.random.default_rng(506).standard_normal(L)[None, :]
+    qkv[:, 2, 0] = np.eye(L)
+    cu = np.array([0, L], dtype=np.int32)
+    got = oracle.attention_ref_varlen_mods(qkv, cu, causal=False, scale=0.4,
+                                           alibi_slopes=np.array([slope], dtype=np.float32))
+    s32 = float(np.float32(slope))
+    w = np.exp(-s32 * np.abs(np.arange(L)[:, None] - np.arange(L)[None, :]))
+    np.testing.assert_allclose(got[:, 0], w / w.sum(axis=1, keepdims=True), atol=1e-13)
+
+
+def test_softcap_limits():
+    """A cap far above the scores changes nothing; scores far above the cap saturate at
+    +-cap, so the weights depend only on the sign of q.k."""
+    qkv, cu = _mods_inputs([10], 2, 4, 507)
+    plain = oracle.attention_ref_varlen(qkv, cu, causal=True, scale=0.5)
+    big = oracle.attention_ref_varlen_mods(qkv, cu, causal=True, scale=0.5, softcap=1e20)
+    np.testing.assert_allclose(big, plain, atol=1e-13)
+    cap = 3.0
+    sat = oracle.attention_ref_varlen_mods(qkv, cu, causal=False, scale=1e12, softcap=cap)
+    for h in range(2):
+        sign = np.sign(qkv[:, 0, h] @ qkv[:, 1, h].T)
+        w = np.exp(cap * sign)
+        ref = (w @ qkv[:, 2, h]) / w.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(sat[:, h], ref, atol=1e-12)
+
+
+def test_mods_tokens_subset_matches_full():
+    qkv, cu = _mods_inputs([13, 4, 20], 2, 5, 508)
+    kw = dict(causal=True, scale=0.45, window=(5, 0), softcap=2.5, alibi_slopes=[0.1, 0.7])
+    full = oracle.attention_ref_varlen_mods(qkv, cu, **kw)
+    toks = np.random.default_rng(509).permutation(37)[:15]
+    part = oracle.attention_ref_varlen_mods(qkv, cu, tokens=toks, **kw)
+    np.testing.assert_array_equal(part, full[toks])
+
+
+def test_mods_validation():
+    qkv, cu = _mods_inputs([4], 2, 3, 510)
+    for kw in (dict(window=(-2, 0)), dict(window=(0, -3)), dict(softcap=-1.0),
+               dict(softcap=float("inf")), dict(alibi_slopes=np.ones(3)),
+               dict(alibi_slopes=np.ones((2, 2)))):
+        with pytest.raises(ValueError):
+            oracle.attention_ref_varlen_mods(qkv, cu, causal=False, scale=1.0, **kw)
+
+
 # ---------------------------------------------------------------- mutation checks
 
 def _pins_pass():
@@ -592,6 +764,12 @@ def _pins_pass():
         lambda: test_decode_brute_force_tiny(0),
         lambda: test_backward_matches_finite_differences(True),
         lambda: test_lse_single_key_and_uniform_scores(),
+        lambda: test_window_zero_returns_own_value(False),
+        lambda: test_window_identical_keys_mean((3, 1)),
+        lambda: test_mods_brute_force_tiny(0),
+        lambda: test_mods_brute_force_tiny(3),
+        lambda: test_alibi_identical_keys_closed_form(),
+        lambda: test_softcap_limits(),
     ]
     for c in checks:
         try:
@@ -624,6 +802,17 @@ def _mut_softmax_sign(S, V):
     return (P @ V) / P.sum(axis=1, keepdims=True)
 
 
+def _window_swapped(rows, n, left, right):
+    rows = np.asarray(rows)[:, None]
+    j = np.arange(n)[None, :]
+    out = np.zeros((rows.shape[0], n), dtype=bool)
+    if right >= 0:
+        out |= j < rows - right
+    if left >= 0:
+        out |= j > rows + left
+    return out
+
+
 MUTANTS = {
     "kv_head_modulo": ("_kv_head", lambda hq, G: hq % max(1, G)),
     "causal_mask_includes_diagonal": ("_causal_masked",
@@ -637,6 +826,19 @@ MUTANTS = {
     "scale_dropped": ("_scale64", lambda s: 1.0),
     "softmax_backward_no_rowsum": ("_softmax_backward", lambda P, dP: P * dP),
     "lse_without_max_shift": ("_lse_rows", lambda S: np.log(np.exp(S).sum(axis=1)) + 1e-3),
+    "window_edge_key_masked": ("_window_masked",
+                               lambda rows, n, left, right: (
+                                   (np.arange(n)[None, :] <= np.asarray(rows)[:, None] - left) if left >= 0
+                                   else np.zeros((len(rows), n), bool)) | (
+                                   (np.arange(n)[None, :] > np.asarray(rows)[:, None] + right) if right >= 0
+                                   else np.zeros((len(rows), n), bool))),
+    "window_sides_swapped": ("_window_masked", _window_swapped),
+    "softcap_factor_dropped": ("_softcap", lambda S, cap: np.tanh(S / cap)),
+    "softcap_inner_scale_dropped": ("_softcap", lambda S, cap: cap * np.tanh(S)),
+    "alibi_sign_flipped": ("_alibi_bias",
+                           lambda rows, n, slope: slope * np.abs(np.asarray(rows)[:, None] - np.arange(n)[None, :])),
+    "alibi_without_abs": ("_alibi_bias",
+                          lambda rows, n, slope: -slope * (np.asarray(rows)[:, None] - np.arange(n)[None, :]).astype(float)),
     "decode_mask_top_left": ("_decode_masked",
                              lambda nq, nk: np.arange(nk)[None, :] > np.arange(nq)[:, None]),
     "decode_mask_includes_next_key": ("_decode_masked",

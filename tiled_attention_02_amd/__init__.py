@@ -220,9 +220,10 @@ def flash_attention(q, k, v, causal: bool = True, scale: float | None = None, ou
 
 
 def flash_attention_backward(q, k, v, out, dout, lse, causal: bool = True,
-                             scale: float | None = None):
+                             scale: float | None = None, grads=None):
     """Gradients (dq, dk, dv) of flash_attention(q, k, v, causal, scale) = out for the output
-    gradient dout, from the lse that flash_attention(..., return_lse=True) returned."""
+    gradient dout, from the lse that flash_attention(..., return_lse=True) returned. ``grads``
+    may give preallocated (dq, dk, dv) buffers of the shapes and dtype of (q, k, v)."""
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out), ("dout", dout), ("lse", lse)):
         _need_gpu_tensor(name, t)
@@ -238,7 +239,14 @@ def flash_attention_backward(q, k, v, out, dout, lse, causal: bool = True,
         raise ValueError("lse must be float32 [B, Hq, N]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if grads is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = grads
+        for name, g, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+            _need_gpu_tensor(name, g)
+            if g.shape != like.shape or g.dtype != like.dtype:
+                raise ValueError(f"{name} must have the shape and dtype of its input")
     st = aule_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
                        lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, Nq,
                        Nk, d, causal, scale, dtype_code(q.dtype), _stream_handle(q.device))

@@ -64,6 +64,12 @@ def dense_inputs(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, *, seed
     return round_to_dtype(q, dtype), round_to_dtype(k, dtype), round_to_dtype(v, dtype)
 
 
+def output_grad(shape, *, seed, dtype="bf16"):
+    """dO for the backward: N(0,1) of the given shape from its own stream of ``seed``."""
+    rng = np.random.default_rng([seed, 1])
+    return round_to_dtype(rng.standard_normal(shape, dtype=np.float32), dtype)
+
+
 def varlen_lengths(num_seqs, lo, hi, *, seed):
     rng = np.random.default_rng(seed)
     return rng.integers(lo, hi, size=num_seqs, endpoint=True), rng
@@ -223,6 +229,27 @@ class DecodeConfig:
                             self.head_dim, seed=self.seed, sigma=self.sigma, dtype=self.dtype)
 
 
+@dataclass(frozen=True)
+class BwdConfig(DenseConfig):
+    """The backward of a dense workload: dQ, dK, dV from Q, K, V, O, dO and the row LSE."""
+
+    def flops(self) -> int:
+        """10*d FLOP per unmasked pair per q head: the recomputed QK^T, dP = dO V^T, dV += P^T dO,
+        dQ += dS K and dK += dS^T Q (five products, 2 FLOP/MAC) — 2.5x the forward."""
+        return 10 * self.head_dim * self.heads_q * self.pairs()
+
+    def bytes_compulsory(self) -> int:
+        """Q, O, dO read and dQ written ([B,Hq,N,d] each); K, V read and dK, dV written
+        ([B,Hkv,N,d] each); the fp32 LSE read."""
+        e = {"f32": 4, "f16": 2, "bf16": 2}[self.dtype]
+        n, d, B = self.seqlen, self.head_dim, self.batch
+        return e * d * n * B * (4 * self.heads_q + 4 * self.heads_kv) + 4 * B * self.heads_q * n
+
+    def grad(self):
+        return output_grad((self.batch, self.heads_q, self.seqlen, self.head_dim), seed=self.seed,
+                           dtype=self.dtype)
+
+
 # The five workloads: a small fp32 case, the A10-shaped fp16 causal case, the bf16 causal
 # GQA case the throughput is quoted on, packed varlen, and a 32k long-context GQA case.
 CONFIGS = {
@@ -246,4 +273,10 @@ C4_LENGTHS = [3336, 409, 787, 1019, 795, 3295, 3569, 2411, 222, 443, 1403, 1810,
 DECODE_CONFIGS = {
     "d1_bf16_decode_gqa": DecodeConfig("d1_bf16_decode_gqa", "bf16", 8, 32, 8, 1, 16384, 128,
                                        True, seed=6),
+}
+
+# The backward of the headline workload (training): same shape, bf16 causal GQA.
+BWD_CONFIGS = {
+    "b1_bf16_causal_gqa_bwd": BwdConfig("b1_bf16_causal_gqa_bwd", "bf16", 4, 32, 8, 4096, 128,
+                                        True, seed=2),
 }
