@@ -144,13 +144,19 @@ def make_step(cfg, dev_inputs, torch):
         out = torch.empty_like(q)
         return lambda: aule.flash_attention(q, k, v, causal=cfg.causal, scale=cfg.softmax_scale,
                                             out=out)
+    from workloads import ModsConfig
     qkv, cu = dev_inputs
     T, _, H, d = qkv.shape
     out = torch.empty((T, H, d), dtype=qkv.dtype, device=qkv.device)
     max_len = int(max(cfg.lengths()))
+    mods = {}
+    if isinstance(cfg, ModsConfig):
+        sl = cfg.slopes()
+        mods = dict(window_size=(cfg.window_left, cfg.window_right), softcap=cfg.softcap,
+                    alibi_slopes=None if sl is None else torch.from_numpy(sl).to("cuda"))
     return lambda: aule.flash_attn_varlen_qkvpacked_func(qkv, cu, max_len,
                                                          softmax_scale=cfg.softmax_scale,
-                                                         causal=cfg.causal, out=out)
+                                                         causal=cfg.causal, out=out, **mods)
 
 
 def time_steps(step, steps, warmup, torch):
@@ -227,15 +233,25 @@ def cpu_baseline(cfg, host_inputs, budget_s):
                 "cores": threads, "kind": "oracle",
                 "sample": f"{done} of {total} (batch, query head) slices, {dt:.1f} s"}
     if not isinstance(cfg, DenseConfig):
+        from workloads import ModsConfig, visible_pairs
         qkv, cu = host_inputs
         t0 = time.perf_counter()
         done_flops, seqs = 0, 0
         for s in range(len(cu) - 1):
             a, e = int(cu[s]), int(cu[s + 1])
             sub_cu = np.array([0, e - a], dtype=np.int32)
-            oracle.attention_ref_varlen(qkv[a:e], sub_cu, causal=cfg.causal, scale=cfg.softmax_scale)
             L = e - a
-            done_flops += 4 * cfg.head_dim * cfg.heads * (L * (L + 1) // 2 if cfg.causal else L * L)
+            if isinstance(cfg, ModsConfig):
+                sl = cfg.slopes()
+                oracle.attention_ref_varlen_mods(qkv[a:e], sub_cu, causal=cfg.causal,
+                                                 scale=cfg.softmax_scale,
+                                                 window=(cfg.window_left, cfg.window_right),
+                                                 softcap=cfg.softcap, alibi_slopes=sl)
+                pairs = visible_pairs(L, cfg.causal, cfg.window_left, cfg.window_right)
+            else:
+                oracle.attention_ref_varlen(qkv[a:e], sub_cu, causal=cfg.causal, scale=cfg.softmax_scale)
+                pairs = L * (L + 1) // 2 if cfg.causal else L * L
+            done_flops += 4 * cfg.head_dim * cfg.heads * pairs
             seqs += 1
             if time.perf_counter() - t0 > budget_s:
                 break
@@ -277,8 +293,9 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
-    from workloads import BWD_CONFIGS, CONFIGS, DECODE_CONFIGS, BwdConfig, DecodeConfig
-    ALL = {**CONFIGS, **DECODE_CONFIGS, **BWD_CONFIGS}
+    from workloads import (BWD_CONFIGS, CONFIGS, DECODE_CONFIGS, MODS_CONFIGS, BwdConfig,
+                           DecodeConfig, ModsConfig)
+    ALL = {**CONFIGS, **DECODE_CONFIGS, **BWD_CONFIGS, **MODS_CONFIGS}
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
@@ -320,6 +337,8 @@ def main():
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": cfg.bytes_compulsory()},
     }
+    if isinstance(cfg, ModsConfig):
+        line["metric"] = "attention varlen fwd with window/softcap/ALiBi TFLOPS (visible pairs) and % of MI355X bf16 MFMA peak"
     if isinstance(cfg, BwdConfig):
         line["metric"] = "attention bwd TFLOPS (causal-adjusted, 2.5x forward FLOPs) and % of MI355X bf16 MFMA peak"
     if isinstance(cfg, DecodeConfig):
@@ -362,8 +381,13 @@ def describe(cfg):
     if isinstance(cfg, DenseConfig):
         return (f"{cfg.dtype} {'causal' if cfg.causal else 'non-causal'} B={cfg.batch} Hq={cfg.heads_q} "
                 f"Hkv={cfg.heads_kv} N={cfg.seqlen} d={cfg.head_dim} scale={cfg.softmax_scale:.6g}")
+    from workloads import ModsConfig
+    extra = ""
+    if isinstance(cfg, ModsConfig):
+        extra = (f" window=({cfg.window_left},{cfg.window_right}) softcap={cfg.softcap:g} "
+                 f"alibi={'geometric' if cfg.alibi else 'off'}")
     return (f"{cfg.dtype} varlen {'causal' if cfg.causal else 'non-causal'} {cfg.num_seqs} seqs "
-            f"L~U[{cfg.len_lo},{cfg.len_hi}] H={cfg.heads} d={cfg.head_dim}")
+            f"L~U[{cfg.len_lo},{cfg.len_hi}] H={cfg.heads} d={cfg.head_dim}{extra}")
 
 
 if __name__ == "__main__":

@@ -104,6 +104,36 @@ aule_status_t aule_attn_fwd_varlen(const void* qkv, const int32_t* cu_seqlens, v
                                    hipStream_t stream);
 
 /*
+ * Varlen attention with score modifiers: the three parameters the varlen signature of the
+ * ewbang.com article lists beside the scale and causal flag (sliding window (left, right),
+ * soft-capping value, ALiBi slopes of shape [heads] or [batch, heads]), fused into the
+ * score step.
+ *
+ * Arguments as aule_attn_fwd_varlen, plus
+ *   window_left, window_right : key j is visible to query i only if j >= i - window_left
+ *                  (when window_left >= 0) and j <= i + window_right (when >= 0), positions
+ *                  counted from the sequence start; -1 = unbounded. With causal,
+ *                  window_right must be -1 or 0 (the causal mask already hides j > i).
+ *   softcap      : > 0 replaces each scaled score x = scale * q_i . k_j by
+ *                  softcap * tanh(x / softcap); 0 = off. Must be finite and >= 0.
+ *   alibi_slopes : NULL = off, else fp32 DEVICE slopes, 4-byte aligned, read only:
+ *                  slope = alibi_slopes[seq * alibi_batch_stride + head], and
+ *                  slope * |i - j| is subtracted from the (capped) score.
+ *   alibi_batch_stride : 0 for [heads] slopes, heads for [batch, heads]; else invalid.
+ * Order: scaled score, soft cap, ALiBi, masks, softmax. With every modifier off this is
+ * aule_attn_fwd_varlen. Errors: INVALID_ARGUMENT for a window size below -1, a positive
+ * window_right with causal, a negative or non-finite softcap, misaligned slopes, a bad
+ * alibi_batch_stride or slopes overlapping o; otherwise as aule_attn_fwd_varlen.
+ */
+aule_status_t aule_attn_fwd_varlen_mods(const void* qkv, const int32_t* cu_seqlens, void* o,
+                                        int32_t num_seqs, int32_t total_tokens,
+                                        int32_t max_seqlen, int32_t heads, int32_t head_dim,
+                                        int32_t causal, float scale, int32_t window_left,
+                                        int32_t window_right, float softcap,
+                                        const float* alibi_slopes, int32_t alibi_batch_stride,
+                                        aule_dtype_t dtype, hipStream_t stream);
+
+/*
  * Attention of a few new queries against a key/value cache (decoding), split over the key
  * range.
  *

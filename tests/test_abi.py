@@ -122,6 +122,34 @@ def test_varlen_empty_problem_is_noop(lib):
     assert varlen(total_tokens=0, qkv=None, cu=None, o=None) == OK
 
 
+def varlen_mods(**kw):
+    a = dict(qkv=P["qkv"], cu=P["cu"], o=P["o"], num_seqs=2, total_tokens=12, max_seqlen=7,
+             heads=2, head_dim=64, causal=1, scale=0.125, wl=4, wr=0, softcap=0.0,
+             alibi=0xD0000000, astride=0, dtype=F16, stream=None)
+    a.update(kw)
+    return aule.aule_attn_fwd_varlen_mods(a["qkv"], a["cu"], a["o"], a["num_seqs"],
+                                          a["total_tokens"], a["max_seqlen"], a["heads"],
+                                          a["head_dim"], a["causal"], a["scale"], a["wl"],
+                                          a["wr"], a["softcap"], a["alibi"], a["astride"],
+                                          a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(wl=-2), INV), (dict(wr=-5, causal=0), INV), (dict(wr=3, causal=1), INV),
+    (dict(softcap=-1.0), INV), (dict(softcap=math.inf), INV), (dict(softcap=math.nan), INV),
+    (dict(alibi=0xD0000002), INV), (dict(astride=1), INV), (dict(astride=-2), INV),
+    (dict(alibi=P["o"] + 16), INV),                       # slopes overlap the output
+    (dict(qkv=None), INV), (dict(head_dim=12), UNS), (dict(num_seqs=0), INV),
+])
+def test_varlen_mods_rejects_invalid_arguments(lib, kw, status):
+    assert varlen_mods(**kw) == status
+    assert aule.aule_last_error() != ""
+
+
+def test_varlen_mods_empty_problem_is_noop(lib):
+    assert varlen_mods(total_tokens=0, qkv=None, cu=None, o=None, alibi=None) == OK
+
+
 def splitkv(**kw):
     a = dict(q=P["q"], k=P["k"], v=P["v"], o=P["o"], batch=2, heads_q=8, heads_kv=2,
              seqlen_q=1, seqlen_k=1000, head_dim=128, causal=1, scale=0.088, dtype=BF16,
@@ -216,8 +244,7 @@ def test_python_wrappers_refuse_cpu_tensors(lib):
         aule.flash_attn_varlen_qkvpacked_func(qkv, cu, 8)
     with pytest.raises(ValueError):
         aule.flash_attention_decode(q, q, q)
-    for kw in (dict(dropout_p=0.1), dict(window_size=(4, 4)), dict(softcap=1.0),
-               dict(alibi_slopes=torch.zeros(2)), dict(return_attn_probs=True)):
+    for kw in (dict(dropout_p=0.1), dict(return_attn_probs=True)):
         with pytest.raises(NotImplementedError):
             aule.flash_attn_varlen_qkvpacked_func(qkv, cu, 8, **kw)
 

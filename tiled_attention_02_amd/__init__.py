@@ -41,6 +41,7 @@ AULE_DTYPE_F32, AULE_DTYPE_F16, AULE_DTYPE_BF16 = 0, 1, 2
 AULE_OK, AULE_ERR_INVALID_ARGUMENT, AULE_ERR_UNSUPPORTED, AULE_ERR_HIP = 0, 1, 2, 3
 
 EXPORTED = ("aule_attn_fwd", "aule_attn_fwd_lse", "aule_attn_bwd", "aule_attn_fwd_varlen",
+            "aule_attn_fwd_varlen_mods",
             "aule_attn_fwd_splitkv", "aule_attn_splitkv_workspace_size", "aule_status_string",
             "aule_last_error")
 
@@ -70,6 +71,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.aule_attn_fwd_varlen.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                          ctypes.c_int, vp]
     lib.aule_attn_fwd_varlen.restype = ctypes.c_int
+    lib.aule_attn_fwd_varlen_mods.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32,
+                                              i32, f32, vp, i32, ctypes.c_int, vp]
+    lib.aule_attn_fwd_varlen_mods.restype = ctypes.c_int
     lib.aule_attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                       ctypes.c_int, vp]
     lib.aule_attn_fwd_lse.restype = ctypes.c_int
@@ -121,6 +125,16 @@ def aule_attn_fwd_varlen(qkv, cu_seqlens, o, num_seqs, total_tokens, max_seqlen,
     return load_library().aule_attn_fwd_varlen(qkv, cu_seqlens, o, num_seqs, total_tokens,
                                                max_seqlen, heads, head_dim, int(causal),
                                                float(scale), int(dtype), stream)
+
+
+def aule_attn_fwd_varlen_mods(qkv, cu_seqlens, o, num_seqs, total_tokens, max_seqlen, heads,
+                              head_dim, causal, scale, window_left, window_right, softcap,
+                              alibi_slopes, alibi_batch_stride, dtype, stream=0) -> int:
+    """Raw call: device pointers as ints (alibi_slopes may be None); returns the status."""
+    return load_library().aule_attn_fwd_varlen_mods(
+        qkv, cu_seqlens, o, num_seqs, total_tokens, max_seqlen, heads, head_dim, int(causal),
+        float(scale), int(window_left), int(window_right), float(softcap), alibi_slopes,
+        int(alibi_batch_stride), int(dtype), stream)
 
 
 def aule_attn_fwd_splitkv(q, k, v, o, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
@@ -300,17 +314,16 @@ def flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen, dropout_p=0.0,
     """Varlen attention over packed qkv [total_tokens, 3, heads, head_dim] with int32
     cu_seqlens [batch+1] on the device; returns [total_tokens, heads, head_dim].
 
+    Score modifiers: ``window_size=(left, right)`` sliding window (-1 = unbounded; with
+    causal, right must be -1 or 0), ``softcap`` > 0 caps the scaled scores at
+    softcap * tanh(x / softcap), ``alibi_slopes`` (fp32 [heads] or [batch, heads] on the
+    device) subtracts slope * |i - j|.
+
     ``validate=True`` also checks cu_seqlens against total_tokens and max_seqlen, which
     reads it back to the host (a synchronisation)."""
     torch = _torch()
     if dropout_p != 0.0:
         raise NotImplementedError("dropout is not supported")
-    if tuple(window_size) != (-1, -1):
-        raise NotImplementedError("window_size is not supported")
-    if softcap != 0.0:
-        raise NotImplementedError("softcap is not supported")
-    if alibi_slopes is not None:
-        raise NotImplementedError("alibi_slopes is not supported")
     if return_attn_probs:
         raise NotImplementedError("return_attn_probs is not supported")
     _need_gpu_tensor("qkv", qkv)
@@ -336,14 +349,35 @@ def flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen, dropout_p=0.0,
         softmax_scale = 1.0 / math.sqrt(d)
     if out is None:
         out = torch.empty((T, H, d), dtype=qkv.dtype, device=qkv.device)
-    st = aule_attn_fwd_varlen(qkv.data_ptr(), cu_seqlens.data_ptr(), out.data_ptr(), num_seqs,
-                              T, int(max_seqlen), H, d, causal, softmax_scale,
-                              dtype_code(qkv.dtype), _stream_handle(qkv.device))
+    wl, wr = (int(window_size[0]), int(window_size[1]))
+    if (wl, wr) == (-1, -1) and softcap == 0.0 and alibi_slopes is None:
+        st = aule_attn_fwd_varlen(qkv.data_ptr(), cu_seqlens.data_ptr(), out.data_ptr(), num_seqs,
+                                  T, int(max_seqlen), H, d, causal, softmax_scale,
+                                  dtype_code(qkv.dtype), _stream_handle(qkv.device))
+        _check(st)
+        return out
+    a_ptr, a_stride = None, 0
+    if alibi_slopes is not None:
+        _need_gpu_tensor("alibi_slopes", alibi_slopes)
+        if alibi_slopes.dtype != torch.float32:
+            raise ValueError("alibi_slopes must be float32")
+        if tuple(alibi_slopes.shape) == (H,):
+            a_stride = 0
+        elif tuple(alibi_slopes.shape) == (num_seqs, H):
+            a_stride = H
+        else:
+            raise ValueError("alibi_slopes must be [heads] or [batch, heads]")
+        a_ptr = alibi_slopes.data_ptr()
+    st = aule_attn_fwd_varlen_mods(qkv.data_ptr(), cu_seqlens.data_ptr(), out.data_ptr(),
+                                   num_seqs, T, int(max_seqlen), H, d, causal, softmax_scale,
+                                   wl, wr, softcap, a_ptr, a_stride, dtype_code(qkv.dtype),
+                                   _stream_handle(qkv.device))
     _check(st)
     return out
 
 
 __all__ = ["aule_attn_fwd", "aule_attn_fwd_lse", "aule_attn_bwd", "aule_attn_fwd_varlen",
+           "aule_attn_fwd_varlen_mods",
            "aule_attn_fwd_splitkv", "flash_attention_backward",
            "aule_attn_splitkv_workspace_size", "aule_status_string", "aule_last_error",
            "flash_attention", "flash_attention_decode", "flash_attn_varlen_qkvpacked_func",

@@ -15,6 +15,13 @@ typedef _Float16 f16_t;
 template <typename T> __device__ __forceinline__ float to_f32(T x) { return static_cast<float>(x); }
 template <typename T> __device__ __forceinline__ T from_f32(float x) { return static_cast<T>(x); }
 
+// cap * tanh(x / cap) for cap > 0, through tanh(y) = 1 - 2 / (exp(2y) + 1): exp2 overflows
+// to +inf for large y (tanh -> 1) and underflows to 0 for very negative y (tanh -> -1).
+__device__ __forceinline__ float soft_cap(float x, float cap, float two_log2e_over_cap) {
+    const float e = __builtin_amdgcn_exp2f(x * two_log2e_over_cap);
+    return cap * (1.f - 2.f * __builtin_amdgcn_rcpf(e + 1.f));
+}
+
 // Where a query tile lives.
 struct TileSlot {
     int valid;       // 0: this workgroup has no work (varlen padding of the grid)

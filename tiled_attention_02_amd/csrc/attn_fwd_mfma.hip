@@ -212,7 +212,8 @@ template <int P> struct Parity { static constexpr int value = P; };
 // PERSIST (dense problems, two buffers): the grid holds one workgroup per CU and each walks
 // several work items, issuing the next item's first K/V tile copy and its Q loads while it
 // finishes the current item, so that their latency and the workgroup launch gap are hidden.
-template <typename T, int D, int WAVES, int NB, int GH, int TB, bool PERSIST, bool CAUSAL, bool VARLEN>
+template <typename T, int D, int WAVES, int NB, int GH, int TB, bool PERSIST, bool CAUSAL, bool VARLEN,
+          bool MODS>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass only needs the launch stub
@@ -273,6 +274,8 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         T* ob;
         float* lseb;                   // this wave's log-sum-exp row (dense, optional)
         i32x4 rk, rv;                  // K / V slice descriptors, exactly the Lk valid rows
+        int kb0;                       // first key walked (score modifiers: window start)
+        float slope;                   // ALiBi slope of this wave's head (score modifiers)
     };
     const int ngroups = p.heads_q / GH;
     const int NG = p.batch * ngroups;
@@ -313,18 +316,31 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         it.qb = static_cast<const T*>(p.q) + (VARLEN ? tok0 * p.q_rstride : bidx * p.q_bstride) + hq * p.q_hstride;
         it.ob = static_cast<T*>(p.o) + (VARLEN ? tok0 * p.o_rstride : bidx * p.o_bstride) + hq * p.o_hstride;
         it.lseb = (!VARLEN && p.lse) ? p.lse + ((int64_t)bidx * p.heads_q + hq) * p.seqlen_q : nullptr;
-        const T* kb = static_cast<const T*>(p.k) + (VARLEN ? tok0 * p.k_rstride : bidx * p.k_bstride) + hk * p.k_hstride;
-        const T* vb = static_cast<const T*>(p.v) + (VARLEN ? tok0 * p.v_rstride : bidx * p.v_bstride) + hk * p.v_hstride;
-        const int k_valid = Lk > 0 ? (int)((int64_t)(Lk - 1) * k_rs + hd * sizeof(T)) : 0;
-        const int v_valid = Lk > 0 ? (int)((int64_t)(Lk - 1) * v_rs + hd * sizeof(T)) : 0;
+        // Score modifiers: a sliding window's left edge lets the walk start at the 32-key
+        // step holding the first key any row of this workgroup sees (the K/V descriptors
+        // start there); the mask works in absolute key positions.
+        int kb0 = 0;
+        it.slope = 0.f;
+        if constexpr (MODS) {
+            if (p.win_left >= 0) kb0 = max(0, tile * BMW - p.win_left) & ~31;
+            if (p.alibi) it.slope = p.alibi[(int64_t)bidx * p.alibi_sstride + hq];
+        }
+        it.kb0 = kb0;
+        const T* kb = static_cast<const T*>(p.k) + (VARLEN ? tok0 * p.k_rstride : bidx * p.k_bstride) + hk * p.k_hstride + kb0 * p.k_rstride;
+        const T* vb = static_cast<const T*>(p.v) + (VARLEN ? tok0 * p.v_rstride : bidx * p.v_bstride) + hk * p.v_hstride + kb0 * p.v_rstride;
+        const int Lk_rel = Lk - kb0;
+        const int k_valid = Lk_rel > 0 ? (int)((int64_t)(Lk_rel - 1) * k_rs + hd * sizeof(T)) : 0;
+        const int v_valid = Lk_rel > 0 ? (int)((int64_t)(Lk_rel - 1) * v_rs + hd * sizeof(T)) : 0;
         it.rk = buffer_desc(kb, k_valid);
         it.rv = buffer_desc(vb, v_valid);
         // The key range is walked in 32-key sub-steps, SPT per K/V tile. All waves of the
         // workgroup walk the same sub-steps (a wave whose own rows end earlier gets fully
         // masked sub-steps at the end, which add exact zeros).
         const int wg_rows_end = min(tile * BMW + BMW, Lq);
-        const int keys_needed = CAUSAL ? wg_rows_end : Lk;
-        it.nsub = (keys_needed + 31) / 32;
+        int keys_needed = CAUSAL ? wg_rows_end : Lk;
+        if constexpr (MODS && !CAUSAL)
+            if (p.win_right >= 0) keys_needed = min(Lk, wg_rows_end + p.win_right);
+        it.nsub = (keys_needed - kb0 + 31) / 32;
         it.n_kt = (it.nsub + SPT - 1) / SPT;
         return true;
     };
@@ -351,6 +367,8 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     // loads before the matrix products).
     const bool neg = p.scale_log2 < 0.f;
     const float c = fmaxf(fabsf(p.scale_log2), 1e-30f);
+    // With score modifiers the mask step leaves the scores in log2 units already.
+    const float cs = MODS ? 1.f : c;
     u32x4 qf[NB][KS];
     // Buffer loads whose descriptor covers the Lq valid rows: rows past the end read as
     // zero, and one lane offset serves all k-steps (a scalar offset adds 32 bytes per step).
@@ -424,8 +442,32 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[nb] = Mfma<T>::mma(kf[ks], qf[nb][ks], acc[nb]);
     };
-    // -inf for keys past the end and (causal) keys after the query; a uniform branch
+    // -inf for keys past the end and (causal) keys after the query; a uniform branch.
+    // With score modifiers every score is rewritten: soft cap and ALiBi bias in natural
+    // units, then log2 units, with the window edges masked too.
+    const float cap = MODS ? p.softcap : 0.f;
+    const float cap_k = cap > 0.f ? 2.f * 1.4426950408889634f / cap : 0.f;
     auto mask = [&](int sub, f32x16 (&acc)[NB]) {
+        if constexpr (MODS) {
+            const int k0 = cur.kb0 + 32 * sub;
+            const float cn = c * 0.69314718055994531f;   // |scale| (Q carries the sign)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int qi = cur.qr0 + 32 * nb + ln;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = k0 + 16 * (r >> 3) + 8 * h + (r & 7);
+                    const bool masked = (key >= cur.Lk) || (CAUSAL && key > qi) ||
+                                        (p.win_left >= 0 && key < qi - p.win_left) ||
+                                        (!CAUSAL && p.win_right >= 0 && key > qi + p.win_right);
+                    float x = acc[nb][r] * cn;
+                    if (cap > 0.f) x = soft_cap(x, cap, cap_k);
+                    x = fmaf(-cur.slope, fabsf((float)(qi - key)), x);
+                    acc[nb][r] = masked ? -INFINITY : x * 1.4426950408889634f;
+                }
+            }
+            return;
+        }
         const int k0 = 32 * sub;
         if ((k0 + 32 > cur.Lk) || (CAUSAL && k0 + 31 > cur.qr0)) {
 #pragma unroll
@@ -475,13 +517,14 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     struct Soft { float m_new[NB], alpha[NB], lsum[NB]; bool raise[NB]; };
     // P = exp2(s * c - m) packed to 16 bit, with its row sum over the rounded values
     auto exp_pack = [&](const f32x16& a, float m, u32x4 (&pf)[2][NB], int nb) {
-        const float mneg = -m;
+        // with a sliding window a row can have no visible key yet (m = -inf): its P are 0
+        const float mneg = (MODS && m == -INFINITY) ? 0.f : -m;
         float lsum = 0.f;
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             float pv8[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) pv8[e] = __builtin_amdgcn_exp2f(fmaf(a[8 * cc + e], c, mneg));
+            for (int e = 0; e < 8; ++e) pv8[e] = __builtin_amdgcn_exp2f(fmaf(a[8 * cc + e], cs, mneg));
             const u32x4 pk = {Mfma<T>::pack2(pv8[0], pv8[1]), Mfma<T>::pack2(pv8[2], pv8[3]),
                               Mfma<T>::pack2(pv8[4], pv8[5]), Mfma<T>::pack2(pv8[6], pv8[7])};
             // the row sum uses the same rounded P that multiplies V, so O stays an exact
@@ -506,7 +549,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 st.lsum[nb] = exp_pack(acc[nb], m_ref[nb], pf, nb);
-                ok = ok && (st.lsum[nb] <= kSlackExp);
+                ok = ok && (st.lsum[nb] <= kSlackExp) && (!MODS || m_ref[nb] != -INFINITY);
             }
             if (__all(ok)) {
 #pragma unroll
@@ -525,12 +568,12 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[nb][r]);
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+            const float mt = (mx == -INFINITY) ? -INFINITY : mx * cs;
             const bool any = __any(mt > m_ref[nb] + kRescaleSlack);
             const float m_new = any ? fmaxf(m_ref[nb], mt) : m_ref[nb];
             st.raise[nb] = any;
             st.m_new[nb] = m_new;
-            st.alpha[nb] = __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
+            st.alpha[nb] = (MODS && m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref[nb] - m_new);
             st.lsum[nb] = exp_pack(acc[nb], m_new, pf, nb);
         }
     };
@@ -704,13 +747,14 @@ int resident_workgroups() {
     return n;
 }
 
-template <typename T, int D, int WAVES, int NB, int GH, int TB, bool PERSIST, bool CAUSAL, bool VARLEN>
+template <typename T, int D, int WAVES, int NB, int GH, int TB, bool PERSIST, bool CAUSAL, bool VARLEN,
+          bool MODS = false>
 hipError_t launch_cfg(const AttnProblem& p, hipStream_t stream) {
     constexpr int BMW = 32 * NB * (WAVES / GH);
     dim3 block(WAVES * 64);
     if constexpr (VARLEN) {
         dim3 grid(varlen_grid_tiles(p.total_tokens, p.batch, BMW), p.heads_q / GH, 1);
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, TB, PERSIST, CAUSAL, true>), grid, block, 0, stream, p, 0);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, TB, PERSIST, CAUSAL, true, MODS>), grid, block, 0, stream, p, 0);
     } else {
         const int n_qtiles = (p.seqlen_q + BMW - 1) / BMW;
         const int64_t nitems = (int64_t)n_qtiles * p.batch * (p.heads_q / GH);
@@ -722,7 +766,7 @@ hipError_t launch_cfg(const AttnProblem& p, hipStream_t stream) {
             if (nblocks > g) nblocks = g;
         }
         dim3 grid((unsigned)nblocks);
-        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, TB, PERSIST, CAUSAL, false>), grid, block, 0, stream, p, n_qtiles);
+        hipLaunchKernelGGL((attn_fwd_mfma_kernel<T, D, WAVES, NB, GH, TB, PERSIST, CAUSAL, false, false>), grid, block, 0, stream, p, n_qtiles);
     }
     return hipGetLastError();
 }
@@ -731,6 +775,9 @@ template <typename T, int D, bool CAUSAL, bool VARLEN>
 hipError_t launch_gh(const AttnProblem& p, hipStream_t stream) {
     const int gh = VARLEN ? 1 : heads_per_group(p.group);
     const int g = gh == 4 ? 2 : gh == 2 ? 1 : 0;
+    if constexpr (VARLEN) {   // score modifiers: 128-key tiles, straight loop
+        if (p.mods) return launch_cfg<T, D, 8, 1, 1, 128, false, CAUSAL, true, true>(p, stream);
+    }
     int form = mfma_loop();
     if (VARLEN && form == 5) form = 1;
     switch (form * 3 + g) {

@@ -24,8 +24,9 @@ constexpr int kBM = 16;
 constexpr int kBN = 32;
 constexpr int kTPR = 8;  // threads per query row
 constexpr int kThreads = kBM * kTPR;
+constexpr float kLog2eF = 1.4426950408889634f;
 
-template <typename T, int DMAX, bool VARLEN>
+template <typename T, int DMAX, bool VARLEN, bool MODS>
 __global__ __launch_bounds__(kThreads) void attn_fwd_valu_kernel(AttnProblem p) {
     __shared__ float sQ[kBM][DMAX + 1];
     __shared__ float sK[kBN][DMAX + 1];
@@ -74,12 +75,21 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_valu_kernel(AttnProblem p) 
     for (int u = 0; u < DMAX / kTPR; ++u) acc[u] = 0.f;
 
     int kend = Lk;
-    if (p.causal) {
-        int last_row = min(row0 + kBM, Lq) - 1;
-        kend = min(Lk, last_row + 1);
+    const int last_row = min(row0 + kBM, Lq) - 1;
+    if (p.causal) kend = min(Lk, last_row + 1);
+    int kbeg = 0;
+    float slope = 0.f, cap = 0.f, cap_k = 0.f;
+    const float scale_nat = p.scale_log2 * 0.69314718055994531f;
+    if constexpr (MODS) {
+        // key tiles entirely outside every row's window are skipped
+        if (p.win_left >= 0) kbeg = max(0, row0 - p.win_left) / kBN * kBN;
+        if (!p.causal && p.win_right >= 0) kend = min(Lk, last_row + 1 + p.win_right);
+        if (p.alibi) slope = p.alibi[(int64_t)slot.seq * p.alibi_sstride + hq];
+        cap = p.softcap;
+        cap_k = cap > 0.f ? 2.f * kLog2eF / cap : 0.f;
     }
 
-    for (int j0 = 0; j0 < kend; j0 += kBN) {
+    for (int j0 = kbeg; j0 < kend; j0 += kBN) {
         __syncthreads();  // previous tile fully consumed (and Q written, first time)
         for (int idx = tid; idx < kBN * DMAX; idx += kThreads) {
             int jj = idx / DMAX, dd = idx % DMAX;
@@ -100,7 +110,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_valu_kernel(AttnProblem p) 
             for (int dd = 0; dd < DMAX; ++dd) dot = fmaf(sQ[r][dd], sK[jj][dd], dot);
             int j = j0 + jj;
             bool masked = (j >= Lk) || (p.causal && j > i);
-            s[u] = masked ? -INFINITY : dot * p.scale_log2;
+            if constexpr (MODS) {
+                masked = masked || (p.win_left >= 0 && j < i - p.win_left) ||
+                         (p.win_right >= 0 && j > i + p.win_right);
+                float x = dot * scale_nat;
+                if (cap > 0.f) x = soft_cap(x, cap, cap_k);
+                x = fmaf(-slope, fabsf((float)(i - j)), x);
+                s[u] = masked ? -INFINITY : x * kLog2eF;
+            } else {
+                s[u] = masked ? -INFINITY : dot * p.scale_log2;
+            }
             tmax = fmaxf(tmax, s[u]);
         }
 #pragma unroll
@@ -148,10 +167,13 @@ hipError_t launch_typed(const AttnProblem& p, hipStream_t stream) {
     dim3 block(kThreads);
     if (p.cu_seqlens) {
         dim3 grid(varlen_grid_tiles(p.total_tokens, p.batch, kBM), p.heads_q, 1);
-        hipLaunchKernelGGL((attn_fwd_valu_kernel<T, DMAX, true>), grid, block, 0, stream, p);
+        if (p.mods)
+            hipLaunchKernelGGL((attn_fwd_valu_kernel<T, DMAX, true, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((attn_fwd_valu_kernel<T, DMAX, true, false>), grid, block, 0, stream, p);
     } else {
         dim3 grid((p.seqlen_q + kBM - 1) / kBM, p.heads_q, p.batch);
-        hipLaunchKernelGGL((attn_fwd_valu_kernel<T, DMAX, false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((attn_fwd_valu_kernel<T, DMAX, false, false>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }

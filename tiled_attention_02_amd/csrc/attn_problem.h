@@ -38,6 +38,16 @@ struct AttnProblem {
     int32_t total_tokens;       // varlen only
     int32_t max_seqlen;         // varlen hint
     float* lse;                 // dense only, optional: per-row log-sum-exp [batch, heads_q, seqlen_q]
+    // Score modifiers (varlen only; read only when `mods` is nonzero). With x the scaled
+    // score in natural units: x <- softcap * tanh(x / softcap) when softcap > 0, then
+    // x <- x - slope * |i - j| with slope = alibi[seq * alibi_sstride + head] when alibi is
+    // set; key j is masked when j < i - win_left (win_left >= 0) or j > i + win_right
+    // (win_right >= 0).
+    int32_t mods;
+    int32_t win_left, win_right;
+    float softcap;
+    const float* alibi;
+    int32_t alibi_sstride;
 };
 
 // Launchers. Each returns hipSuccess or the launch error; none synchronises.

@@ -205,6 +205,78 @@ aule_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, flo
 
 }  // namespace
 
+namespace {
+
+struct VarlenMods {
+    int32_t win_left = -1, win_right = -1;
+    float softcap = 0.f;
+    const float* alibi = nullptr;
+    int32_t alibi_sstride = 0;
+};
+
+aule_status_t varlen_impl(const void* qkv, const int32_t* cu_seqlens, void* o, int32_t num_seqs,
+                          int32_t total_tokens, int32_t max_seqlen, int32_t heads,
+                          int32_t head_dim, int32_t causal, float scale, aule_dtype_t dtype,
+                          const VarlenMods& mods, hipStream_t stream) {
+    if (total_tokens < 0 || max_seqlen < 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "total_tokens and max_seqlen must be >= 0");
+    if (num_seqs <= 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "num_seqs must be positive (got %d)", num_seqs);
+    if (heads <= 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "heads must be positive");
+    if (aule_status_t st = check_common(head_dim, scale, dtype)) return st;
+    if (total_tokens == 0) {
+        g_last_error[0] = '\0';
+        return AULE_OK;  // every sequence is empty
+    }
+    if (!qkv || !cu_seqlens || !o)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "null pointer");
+    if (!aligned16(qkv) || !aligned16(o) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "qkv/o must be 16-byte aligned, cu_seqlens 4-byte aligned");
+    const size_t es = elem_size(dtype);
+    const size_t nqkv = (size_t)total_tokens * 3 * heads * head_dim * es;
+    const size_t no = (size_t)total_tokens * heads * head_dim * es;
+    if (overlaps(o, no, qkv, nqkv) || overlaps(o, no, cu_seqlens, (size_t)(num_seqs + 1) * 4))
+        return fail(AULE_ERR_INVALID_ARGUMENT, "output overlaps an input");
+    if ((int64_t)total_tokens + num_seqs > INT32_MAX)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "too many tokens");
+
+    const int64_t hd = (int64_t)heads * head_dim;
+    const char* base = static_cast<const char*>(qkv);
+    aule::AttnProblem p{};
+    p.q = base;
+    p.k = base + hd * es;
+    p.v = base + 2 * hd * es;
+    p.o = o;
+    p.q_rstride = p.k_rstride = p.v_rstride = 3 * hd;
+    p.q_hstride = p.k_hstride = p.v_hstride = head_dim;
+    p.q_bstride = p.k_bstride = p.v_bstride = 0;
+    p.o_rstride = hd; p.o_hstride = head_dim; p.o_bstride = 0;
+    p.batch = num_seqs; p.heads_q = heads; p.heads_kv = heads; p.group = 1;
+    p.seqlen_q = max_seqlen; p.seqlen_k = max_seqlen; p.head_dim = head_dim;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = scale * kLog2e;
+    p.cu_seqlens = cu_seqlens;
+    p.total_tokens = total_tokens;
+    p.max_seqlen = max_seqlen;
+    // causal already hides every key after the query: only a left edge remains
+    const int32_t wr = causal ? -1 : mods.win_right;
+    p.mods = (mods.win_left >= 0 || wr >= 0 || mods.softcap > 0.f || mods.alibi) ? 1 : 0;
+    p.win_left = mods.win_left;
+    p.win_right = wr;
+    p.softcap = mods.softcap;
+    p.alibi = mods.alibi;
+    p.alibi_sstride = mods.alibi_sstride;
+    if (p.alibi) {
+        const size_t na = ((size_t)(num_seqs - 1) * mods.alibi_sstride + heads) * sizeof(float);
+        if (overlaps(o, no, p.alibi, na))
+            return fail(AULE_ERR_INVALID_ARGUMENT, "output overlaps alibi_slopes");
+    }
+    return dispatch(p, dtype, stream);
+}
+
+}  // namespace
+
 extern "C" {
 
 aule_status_t aule_attn_fwd(const void* q, const void* k, const void* v, void* o,
@@ -306,48 +378,37 @@ aule_status_t aule_attn_fwd_varlen(const void* qkv, const int32_t* cu_seqlens, v
                                    int32_t max_seqlen, int32_t heads, int32_t head_dim,
                                    int32_t causal, float scale, aule_dtype_t dtype,
                                    hipStream_t stream) {
-    if (total_tokens < 0 || max_seqlen < 0)
-        return fail(AULE_ERR_INVALID_ARGUMENT, "total_tokens and max_seqlen must be >= 0");
-    if (num_seqs <= 0)
-        return fail(AULE_ERR_INVALID_ARGUMENT, "num_seqs must be positive (got %d)", num_seqs);
-    if (heads <= 0)
-        return fail(AULE_ERR_INVALID_ARGUMENT, "heads must be positive");
-    if (aule_status_t st = check_common(head_dim, scale, dtype)) return st;
-    if (total_tokens == 0) {
-        g_last_error[0] = '\0';
-        return AULE_OK;  // every sequence is empty
-    }
-    if (!qkv || !cu_seqlens || !o)
-        return fail(AULE_ERR_INVALID_ARGUMENT, "null pointer");
-    if (!aligned16(qkv) || !aligned16(o) || (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u))
-        return fail(AULE_ERR_INVALID_ARGUMENT, "qkv/o must be 16-byte aligned, cu_seqlens 4-byte aligned");
-    const size_t es = elem_size(dtype);
-    const size_t nqkv = (size_t)total_tokens * 3 * heads * head_dim * es;
-    const size_t no = (size_t)total_tokens * heads * head_dim * es;
-    if (overlaps(o, no, qkv, nqkv) || overlaps(o, no, cu_seqlens, (size_t)(num_seqs + 1) * 4))
-        return fail(AULE_ERR_INVALID_ARGUMENT, "output overlaps an input");
-    if ((int64_t)total_tokens + num_seqs > INT32_MAX)
-        return fail(AULE_ERR_INVALID_ARGUMENT, "too many tokens");
+    return varlen_impl(qkv, cu_seqlens, o, num_seqs, total_tokens, max_seqlen, heads, head_dim,
+                       causal, scale, dtype, VarlenMods{}, stream);
+}
 
-    const int64_t hd = (int64_t)heads * head_dim;
-    const char* base = static_cast<const char*>(qkv);
-    aule::AttnProblem p{};
-    p.q = base;
-    p.k = base + hd * es;
-    p.v = base + 2 * hd * es;
-    p.o = o;
-    p.q_rstride = p.k_rstride = p.v_rstride = 3 * hd;
-    p.q_hstride = p.k_hstride = p.v_hstride = head_dim;
-    p.q_bstride = p.k_bstride = p.v_bstride = 0;
-    p.o_rstride = hd; p.o_hstride = head_dim; p.o_bstride = 0;
-    p.batch = num_seqs; p.heads_q = heads; p.heads_kv = heads; p.group = 1;
-    p.seqlen_q = max_seqlen; p.seqlen_k = max_seqlen; p.head_dim = head_dim;
-    p.causal = causal ? 1 : 0;
-    p.scale_log2 = scale * kLog2e;
-    p.cu_seqlens = cu_seqlens;
-    p.total_tokens = total_tokens;
-    p.max_seqlen = max_seqlen;
-    return dispatch(p, dtype, stream);
+aule_status_t aule_attn_fwd_varlen_mods(const void* qkv, const int32_t* cu_seqlens, void* o,
+                                        int32_t num_seqs, int32_t total_tokens,
+                                        int32_t max_seqlen, int32_t heads, int32_t head_dim,
+                                        int32_t causal, float scale, int32_t window_left,
+                                        int32_t window_right, float softcap,
+                                        const float* alibi_slopes, int32_t alibi_batch_stride,
+                                        aule_dtype_t dtype, hipStream_t stream) {
+    if (window_left < -1 || window_right < -1)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "window sizes must be >= -1 (got %d, %d)", window_left, window_right);
+    if (causal && window_right > 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "causal attention takes window_right -1 or 0 (got %d)", window_right);
+    if (!std::isfinite(softcap) || softcap < 0.f)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "softcap must be finite and >= 0");
+    if (alibi_slopes) {
+        if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
+            return fail(AULE_ERR_INVALID_ARGUMENT, "alibi_slopes must be 4-byte aligned");
+        if (alibi_batch_stride != 0 && alibi_batch_stride != heads)
+            return fail(AULE_ERR_INVALID_ARGUMENT, "alibi_batch_stride must be 0 ([heads]) or heads ([batch, heads])");
+    }
+    VarlenMods m;
+    m.win_left = window_left;
+    m.win_right = window_right;
+    m.softcap = softcap;
+    m.alibi = alibi_slopes;
+    m.alibi_sstride = alibi_slopes ? alibi_batch_stride : 0;
+    return varlen_impl(qkv, cu_seqlens, o, num_seqs, total_tokens, max_seqlen, heads, head_dim,
+                       causal, scale, dtype, m, stream);
 }
 
 aule_status_t aule_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,

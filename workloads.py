@@ -189,6 +189,35 @@ class VarlenConfig:
         return qkv, cu
 
 
+def alibi_slopes(heads: int) -> np.ndarray:
+    """Geometric ALiBi slopes 2^(-8 (h + 1) / heads), fp32 [heads]."""
+    return (2.0 ** (-8.0 * (np.arange(heads) + 1) / heads)).astype(np.float32)
+
+
+def visible_pairs(L: int, causal: bool, left: int, right: int) -> int:
+    """Unmasked (query, key) pairs of one sequence of length L under causal / window."""
+    i = np.arange(L, dtype=np.int64)
+    hi = i if causal else (np.minimum(L - 1, i + right) if right >= 0 else np.full(L, L - 1))
+    lo = np.maximum(0, i - left) if left >= 0 else np.zeros(L, dtype=np.int64)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+@dataclass(frozen=True)
+class ModsConfig(VarlenConfig):
+    """A varlen workload with score modifiers (sliding window, soft cap, ALiBi)."""
+    window_left: int = -1
+    window_right: int = -1
+    softcap: float = 0.0
+    alibi: bool = False
+
+    def pairs(self) -> int:
+        return sum(visible_pairs(int(l), self.causal, self.window_left, self.window_right)
+                   for l in self.lengths())
+
+    def slopes(self):
+        return alibi_slopes(self.heads) if self.alibi else None
+
+
 @dataclass(frozen=True)
 class DecodeConfig:
     """A few new queries per sequence against a key/value cache (causal: the queries are the
@@ -279,4 +308,12 @@ DECODE_CONFIGS = {
 BWD_CONFIGS = {
     "b1_bf16_causal_gqa_bwd": BwdConfig("b1_bf16_causal_gqa_bwd", "bf16", 4, 32, 8, 4096, 128,
                                         True, seed=2),
+}
+
+# The varlen workload with all three score modifiers on: a 1024-key sliding window (causal),
+# a soft cap of 50 on the scaled scores and geometric ALiBi slopes.
+MODS_CONFIGS = {
+    "m1_bf16_varlen_mods": ModsConfig("m1_bf16_varlen_mods", "bf16", 16, 64, 4096, 16, 128, True,
+                                      seed=3, window_left=1024, window_right=0, softcap=50.0,
+                                      alibi=True),
 }
