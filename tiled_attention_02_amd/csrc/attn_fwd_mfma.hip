@@ -443,27 +443,44 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
             for (int nb = 0; nb < NB; ++nb) acc[nb] = Mfma<T>::mma(kf[ks], qf[nb][ks], acc[nb]);
     };
     // -inf for keys past the end and (causal) keys after the query; a uniform branch.
-    // With score modifiers every score is rewritten: soft cap and ALiBi bias in natural
-    // units, then log2 units, with the window edges masked too.
+    // With score modifiers every score is rewritten into log2 units: soft cap
+    // cap*log2(e)*tanh(x/cap) = cap_l2 - 2 cap_l2 / (exp2(2 x log2(e) / cap) + 1) with
+    // x = |scale| q.k (Q carries the sign of the scale), then the ALiBi bias; the masks
+    // (sequence end, causal, window edges) only on sub-steps that straddle an edge.
     const float cap = MODS ? p.softcap : 0.f;
-    const float cap_k = cap > 0.f ? 2.f * 1.4426950408889634f / cap : 0.f;
+    const float cap_l2 = cap * 1.4426950408889634f;
+    const float cap_k = cap > 0.f ? 2.f * c / cap : 0.f;
     auto mask = [&](int sub, f32x16 (&acc)[NB]) {
         if constexpr (MODS) {
             const int k0 = cur.kb0 + 32 * sub;
-            const float cn = c * 0.69314718055994531f;   // |scale| (Q carries the sign)
+            const int qlo = cur.qr0, qhi = cur.qr0 + 32 * NB - 1;
+            const bool edge = (k0 + 32 > cur.Lk) || (CAUSAL && k0 + 31 > qlo) ||
+                              (p.win_left >= 0 && k0 < qhi - p.win_left) ||
+                              (!CAUSAL && p.win_right >= 0 && k0 + 31 > qlo + p.win_right);
+            const float slope_l2 = cur.slope * 1.4426950408889634f;
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const int qi = cur.qr0 + 32 * nb + ln;
+                const int qi = qlo + 32 * nb + ln;
+                const float fb = (float)(qi - k0 - 8 * h);   // qi - key = fb - (key offset)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + 16 * (r >> 3) + 8 * h + (r & 7);
-                    const bool masked = (key >= cur.Lk) || (CAUSAL && key > qi) ||
-                                        (p.win_left >= 0 && key < qi - p.win_left) ||
-                                        (!CAUSAL && p.win_right >= 0 && key > qi + p.win_right);
-                    float x = acc[nb][r] * cn;
-                    if (cap > 0.f) x = soft_cap(x, cap, cap_k);
-                    x = fmaf(-cur.slope, fabsf((float)(qi - key)), x);
-                    acc[nb][r] = masked ? -INFINITY : x * 1.4426950408889634f;
+                    const int koff_r = 16 * (r >> 3) + (r & 7);
+                    float x;
+                    if (cap > 0.f) {
+                        const float e = __builtin_amdgcn_exp2f(acc[nb][r] * cap_k);
+                        x = fmaf(-2.f * cap_l2, __builtin_amdgcn_rcpf(e + 1.f), cap_l2);
+                    } else {
+                        x = acc[nb][r] * c;
+                    }
+                    if (slope_l2 != 0.f) x = fmaf(-slope_l2, fabsf(fb - (float)koff_r), x);
+                    if (edge) {
+                        const int key = k0 + 8 * h + koff_r;
+                        const bool masked = (key >= cur.Lk) || (CAUSAL && key > qi) ||
+                                            (p.win_left >= 0 && key < qi - p.win_left) ||
+                                            (!CAUSAL && p.win_right >= 0 && key > qi + p.win_right);
+                        x = masked ? -INFINITY : x;
+                    }
+                    acc[nb][r] = x;
                 }
             }
             return;
