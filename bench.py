@@ -30,6 +30,7 @@ HBM_PEAK_GBS = 8000.0
 # Sources each workload's kernels are built from: a traffic record taken on other sources is
 # stale and not reported.
 KERNEL_SOURCES = ["tiled_attention_02_amd/csrc/attn_fwd_mfma.hip",
+                  "tiled_attention_02_amd/csrc/attn_mfma.h",
                   "tiled_attention_02_amd/csrc/attn_device.h",
                   "tiled_attention_02_amd/csrc/attn_problem.h",
                   "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
@@ -37,8 +38,10 @@ DECODE_SOURCES = ["tiled_attention_02_amd/csrc/attn_decode.hip",
                   "tiled_attention_02_amd/csrc/attn_decode.h",
                   "tiled_attention_02_amd/csrc/attn_device.h",
                   "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
-BWD_SOURCES = ["tiled_attention_02_amd/csrc/attn_bwd.hip",
+BWD_SOURCES = ["tiled_attention_02_amd/csrc/attn_bwd_mfma.hip",
+               "tiled_attention_02_amd/csrc/attn_bwd.hip",
                "tiled_attention_02_amd/csrc/attn_bwd.h",
+               "tiled_attention_02_amd/csrc/attn_mfma.h",
                "tiled_attention_02_amd/csrc/attn_device.h",
                "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")

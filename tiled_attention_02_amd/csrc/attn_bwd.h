@@ -33,7 +33,9 @@ struct BwdProblem {
     float scale;
 };
 
-// Launches the dK/dV and dQ kernels on `stream`; does not synchronise.
+// Launches the dK/dV and dQ kernels on `stream`; does not synchronise. The vector-ALU
+// kernels take every dtype; the matrix-core kernels take fp16 and bf16.
 hipError_t launch_attn_bwd(const BwdProblem& p, Dtype dt, hipStream_t stream);
+hipError_t launch_attn_bwd_mfma(const BwdProblem& p, Dtype dt, hipStream_t stream);
 
 }  // namespace aule

@@ -1,0 +1,355 @@
+// Attention backward (dQ, dK, dV) on the matrix cores, fp16/bf16 inputs, fp32 accumulation.
+//
+// The score matrix is recomputed tile by tile from Q, K and the forward's per-row
+// log-sum-exp (FlashAttention-T commentary, ai-stack.site, FAQ 4, training bullet). Per
+// (query i, key j) pair: P = exp2(scale log2(e) q_i.k_j - LSE_i log2(e)) (0 where masked),
+// dP = do_i.v_j, dS = P (dP - D_i) with D_i = do_i.o_i; dV_j += P dO_i,
+// dK_j += scale dS q_i, dQ_i += scale dS k_j.
+//
+// Two kernels, no atomics (deterministic), 4 waves per workgroup, 32-row / 32-key steps:
+//   * dK/dV: wave w owns 32 keys (K and V rows held as B operands in registers) and the
+//     transposed accumulators dK^T, dV^T (d x 32 keys). The workgroup walks every query
+//     head of its GQA group and every 32-row query tile (causal: from its first key on);
+//     Q and dO tiles go through LDS (double-buffered, the next tile's global loads issued
+//     before the current tile's products), D_i is formed from the O and dO chunks as they
+//     arrive. Per tile: S = Q K^T and dP = dO V^T with Q / dO rows fed in sigma order, so
+//     P and dS leave the accumulators already in the B-operand layout of
+//     dV^T += dO^T P and dK^T += Q^T dS, whose A operands (dO^T, Q^T) are transposing LDS
+//     reads (ds_read_b64_tr_b16).
+//   * dQ: wave w owns 32 query rows (Q and dO rows in registers, LSE_i and D_i per lane);
+//     the workgroup walks the key tiles (causal: up to its last row). Per tile: S^T = K Q^T,
+//     dP^T = V dO^T with K / V rows in sigma order, then dQ^T += K^T dS^T with K^T read
+//     transposed from LDS.
+// LDS tiles are row-major [32][D] with one 16-byte pad per row.
+#include <hip/hip_runtime.h>
+
+#include "attn_bwd.h"
+#include "attn_mfma.h"
+
+namespace aule {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr float kLog2eF = 1.4426950408889634f;
+
+template <int D>
+struct Tile {
+    static constexpr int RS = D * 2 + 16;                 // bytes per LDS row
+    static constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    static constexpr int BYTES = 32 * RS;
+    static constexpr int NCH = 32 * CPR / kThreads;       // chunks per thread per tile
+    static constexpr int KS = D / 16;                     // k-steps over head_dim
+    static constexpr int DB = D / 32;                     // 32-row blocks of head_dim
+    static_assert(NCH >= 1 && NCH * kThreads == 32 * CPR, "tile chunks must split evenly");
+};
+
+// Rows [r0, r0 + 32) of a [rows, d] slice as 16-byte chunks, this thread's share (zero past
+// the last row and past head_dim).
+template <typename T, int D>
+__device__ __forceinline__ void fetch_rows(u32x4 (&c)[Tile<D>::NCH], const T* base, int r0, int rows, int d) {
+#pragma unroll
+    for (int i = 0; i < Tile<D>::NCH; ++i) {
+        const int idx = (int)threadIdx.x + kThreads * i;
+        const int row = idx / Tile<D>::CPR, ch = idx % Tile<D>::CPR;
+        const int r = r0 + row;
+        c[i] = (r < rows && ch * 8 < d) ? *reinterpret_cast<const u32x4*>(base + (int64_t)r * d + ch * 8)
+                                        : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+template <int D>
+__device__ __forceinline__ void put_rows(char* tile, const u32x4 (&c)[Tile<D>::NCH]) {
+#pragma unroll
+    for (int i = 0; i < Tile<D>::NCH; ++i) {
+        const int idx = (int)threadIdx.x + kThreads * i;
+        *reinterpret_cast<u32x4*>(tile + (idx / Tile<D>::CPR) * Tile<D>::RS + (idx % Tile<D>::CPR) * 16) = c[i];
+    }
+}
+
+// A operand with rows in sigma order: lane l supplies row sigma(l % 32), k-chunk 2ks + h.
+template <int D>
+__device__ __forceinline__ u32x4 rd_rows(const char* tile, int ks, int lane) {
+    return *reinterpret_cast<const u32x4*>(tile + sigma(lane & 31) * Tile<D>::RS + (2 * ks + (lane >> 5)) * 16);
+}
+// A operand of a transposed tile: A[m = column 32db + l % 32][k = row 16kk + 8h .. + 7],
+// two transposing 8-byte reads (each 16-lane group reads 4 rows x 16 columns).
+template <int D>
+__device__ __forceinline__ u32x4 rd_cols(const char* tile, int db, int kk, int lane) {
+    const int tg = lane >> 4, tc = lane & 15;
+    const int row0 = 16 * kk + 8 * (tg >> 1) + (tc >> 2);
+    const int coff = (4 * db + 2 * (tg & 1) + ((tc & 3) >> 1)) * 16 + (tc & 1) * 8;
+    u32x4 out;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const char* addr = tile + (row0 + 4 * t) * Tile<D>::RS + coff;
+        const i16x4_t part = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<char*>(addr)));
+        const u32x2 w = __builtin_bit_cast(u32x2, part);
+        out[2 * t] = w[0];
+        out[2 * t + 1] = w[1];
+    }
+    return out;
+}
+
+// One row (this lane's) of a [rows, d] slice as B-operand chunks: chunk 2ks + h of row r.
+template <typename T, int D>
+__device__ __forceinline__ void fetch_operand(u32x4 (&f)[Tile<D>::KS], const T* base, int r, int rows, int d, int h) {
+#pragma unroll
+    for (int ks = 0; ks < Tile<D>::KS; ++ks) {
+        const int col = (2 * ks + h) * 8;
+        f[ks] = (r < rows && col < d) ? *reinterpret_cast<const u32x4*>(base + (int64_t)r * d + col)
+                                      : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// Transposed accumulators (register r of block db: column 32db + 8(r/4) + 4h + r%4 of this
+// lane's row) scaled and rounded to T, four consecutive columns per 8-byte store.
+template <typename T, int D>
+__device__ __forceinline__ void store_rowT(T* row, const f32x16 (&acc)[Tile<D>::DB], float mul, int d, int h) {
+#pragma unroll
+    for (int db = 0; db < Tile<D>::DB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const int c0 = 32 * db + 8 * q4 + 4 * h;
+            if (c0 < d) {
+                const u32x2 w = {Mfma<T>::pack2(acc[db][4 * q4] * mul, acc[db][4 * q4 + 1] * mul),
+                                 Mfma<T>::pack2(acc[db][4 * q4 + 2] * mul, acc[db][4 * q4 + 3] * mul)};
+                *reinterpret_cast<u32x2*>(row + c0) = w;
+            }
+        }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
+    using TL = Tile<D>;
+    __shared__ __attribute__((aligned(16))) char sQ[2][TL::BYTES];
+    __shared__ __attribute__((aligned(16))) char sdO[2][TL::BYTES];
+    __shared__ __attribute__((aligned(16))) float sL[2][32];
+    __shared__ __attribute__((aligned(16))) float sD[2][32];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, ln = lane & 31;
+    const int Nq = p.seqlen_q, Nk = p.seqlen_k, d = p.head_dim, G = p.group;
+    const int j0 = blockIdx.x * 32 * kWaves, hk = blockIdx.y, b = blockIdx.z;
+    const int key = j0 + 32 * wave + ln;                 // this lane's key (B-operand column)
+    const int64_t kv_off = ((int64_t)b * p.heads_kv + hk) * Nk * d;
+    // work: (query head g of the group, 32-row query tile), causal from the first key on.
+    // With no query rows (nit == 0) only the zero gradients are written: q, k, v, o, do and
+    // lse may then be null and are not read.
+    const int i_start = p.causal ? j0 : 0;
+    const int ntile = Nq > i_start ? (Nq - i_start + 31) / 32 : 0;
+    const int nit = G * ntile;
+
+    u32x4 kf[TL::KS], vf[TL::KS];
+    if (nit > 0) {
+        fetch_operand<T, D>(kf, static_cast<const T*>(p.k) + kv_off, key, Nk, d, h);
+        fetch_operand<T, D>(vf, static_cast<const T*>(p.v) + kv_off, key, Nk, d, h);
+    }
+
+    f32x16 dk[TL::DB], dv[TL::DB];
+#pragma unroll
+    for (int db = 0; db < TL::DB; ++db) { dk[db] = f32x16{}; dv[db] = f32x16{}; }
+    const float c2 = p.scale * kLog2eF;
+
+    u32x4 cq[TL::NCH], cdo[TL::NCH], co[TL::NCH];
+    float lse_v = 0.f;
+    auto fetch = [&](int it) {
+        const int g = it / ntile, i0 = i_start + 32 * (it - g * ntile);
+        const int64_t bh = (int64_t)b * p.heads_q + hk * G + g;
+        const int64_t q_off = bh * Nq * d;
+        fetch_rows<T, D>(cq, static_cast<const T*>(p.q) + q_off, i0, Nq, d);
+        fetch_rows<T, D>(cdo, static_cast<const T*>(p.do_) + q_off, i0, Nq, d);
+        fetch_rows<T, D>(co, static_cast<const T*>(p.o) + q_off, i0, Nq, d);
+        const int r = i0 + (int)threadIdx.x;
+        lse_v = (threadIdx.x < 32 && r < Nq) ? p.lse[bh * Nq + r] : 0.f;
+    };
+    auto commit = [&](int buf) {
+        put_rows<D>(sQ[buf], cq);
+        put_rows<D>(sdO[buf], cdo);
+        // D_i = do_i . o_i: a chunk pair per thread, summed over the CPR chunks of a row
+        // (consecutive lanes)
+#pragma unroll
+        for (int i = 0; i < TL::NCH; ++i) {
+            float x = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) x = Mfma<T>::dot2(cdo[i][w], co[i][w], x);
+#pragma unroll
+            for (int off = 1; off < TL::CPR; off <<= 1) x += __shfl_xor(x, off);
+            const int idx = (int)threadIdx.x + kThreads * i;
+            if (idx % TL::CPR == 0) sD[buf][idx / TL::CPR] = x;
+        }
+        if (threadIdx.x < 32) sL[buf][threadIdx.x] = lse_v * kLog2eF;
+    };
+
+    if (nit > 0) {
+        fetch(0);
+        commit(0);
+    }
+    __syncthreads();
+    for (int it = 0; it < nit; ++it) {
+        const int buf = it & 1;
+        const int g = it / ntile, i0 = i_start + 32 * (it - g * ntile);
+        if (it + 1 < nit) fetch(it + 1);
+        // S = Q K^T, dP = dO V^T: register r holds query i0 + 16(r/8) + 8h + r%8, key `key`
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < TL::KS; ++ks) {
+            s = Mfma<T>::mma(rd_rows<D>(sQ[buf], ks, lane), kf[ks], s);
+            dp = Mfma<T>::mma(rd_rows<D>(sdO[buf], ks, lane), vf[ks], dp);
+        }
+        u32x4 pf[2], dsf[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int q0 = 16 * kk + 8 * h;
+            float pv[8], dsv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int qi = i0 + q0 + e;
+                const bool vis = qi < Nq && key < Nk && (!p.causal || key <= qi);
+                const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -sL[buf][q0 + e])) : 0.f;
+                pv[e] = pe;
+                dsv[e] = pe * (dp[8 * kk + e] - sD[buf][q0 + e]);
+            }
+            pf[kk] = u32x4{Mfma<T>::pack2(pv[0], pv[1]), Mfma<T>::pack2(pv[2], pv[3]),
+                           Mfma<T>::pack2(pv[4], pv[5]), Mfma<T>::pack2(pv[6], pv[7])};
+            dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
+                            Mfma<T>::pack2(dsv[4], dsv[5]), Mfma<T>::pack2(dsv[6], dsv[7])};
+        }
+        // dV^T += dO^T P, dK^T += Q^T dS
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < TL::DB; ++db) {
+                dv[db] = Mfma<T>::mma(rd_cols<D>(sdO[buf], db, kk, lane), pf[kk], dv[db]);
+                dk[db] = Mfma<T>::mma(rd_cols<D>(sQ[buf], db, kk, lane), dsf[kk], dk[db]);
+            }
+        if (it + 1 < nit) commit(buf ^ 1);
+        __syncthreads();
+    }
+    if (key < Nk) {
+        store_rowT<T, D>(static_cast<T*>(p.dk) + kv_off + (int64_t)key * d, dk, p.scale, d, h);
+        store_rowT<T, D>(static_cast<T*>(p.dv) + kv_off + (int64_t)key * d, dv, 1.f, d, h);
+    }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void attn_bwd_dq_mfma_kernel(BwdProblem p) {
+    using TL = Tile<D>;
+    __shared__ __attribute__((aligned(16))) char sK[2][TL::BYTES];
+    __shared__ __attribute__((aligned(16))) char sV[2][TL::BYTES];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, ln = lane & 31;
+    const int Nq = p.seqlen_q, Nk = p.seqlen_k, d = p.head_dim;
+    const int i0 = blockIdx.x * 32 * kWaves, hq = blockIdx.y, b = blockIdx.z;
+    const int hk = hq / p.group;
+    const int qi = i0 + 32 * wave + ln;                  // this lane's query (B-operand column)
+    const int64_t bh = (int64_t)b * p.heads_q + hq;
+    const int64_t q_off = bh * Nq * d;
+    const int64_t kv_off = ((int64_t)b * p.heads_kv + hk) * Nk * d;
+    const T* Kb = static_cast<const T*>(p.k) + kv_off;
+    const T* Vb = static_cast<const T*>(p.v) + kv_off;
+
+    u32x4 qf[TL::KS], dof[TL::KS];
+    fetch_operand<T, D>(qf, static_cast<const T*>(p.q) + q_off, qi, Nq, d, h);
+    fetch_operand<T, D>(dof, static_cast<const T*>(p.do_) + q_off, qi, Nq, d, h);
+    float delta;
+    {
+        u32x4 of[TL::KS];
+        fetch_operand<T, D>(of, static_cast<const T*>(p.o) + q_off, qi, Nq, d, h);
+        float x = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < TL::KS; ++ks)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) x = Mfma<T>::dot2(dof[ks][w], of[ks][w], x);
+        delta = x + __shfl_xor(x, 32);                    // the other half of the row
+    }
+    const float lse2 = qi < Nq ? p.lse[bh * Nq + qi] * kLog2eF : 0.f;
+    const float c2 = p.scale * kLog2eF;
+
+    f32x16 dq[TL::DB];
+#pragma unroll
+    for (int db = 0; db < TL::DB; ++db) dq[db] = f32x16{};
+
+    const int j_end = p.causal ? min(Nk, i0 + 32 * kWaves) : Nk;
+    const int nkt = (j_end + 31) / 32;
+    u32x4 ck[TL::NCH], cv[TL::NCH];
+    auto fetch = [&](int t) {
+        fetch_rows<T, D>(ck, Kb, 32 * t, Nk, d);
+        fetch_rows<T, D>(cv, Vb, 32 * t, Nk, d);
+    };
+    auto commit = [&](int buf) {
+        put_rows<D>(sK[buf], ck);
+        put_rows<D>(sV[buf], cv);
+    };
+    if (nkt > 0) {
+        fetch(0);
+        commit(0);
+    }
+    __syncthreads();
+    for (int t = 0; t < nkt; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < nkt) fetch(t + 1);
+        // S^T = K Q^T, dP^T = V dO^T: register r holds key 32t + 16(r/8) + 8h + r%8, query qi
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < TL::KS; ++ks) {
+            s = Mfma<T>::mma(rd_rows<D>(sK[buf], ks, lane), qf[ks], s);
+            dp = Mfma<T>::mma(rd_rows<D>(sV[buf], ks, lane), dof[ks], dp);
+        }
+        u32x4 dsf[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            float dsv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int kj = 32 * t + 16 * kk + 8 * h + e;
+                const bool vis = qi < Nq && kj < Nk && (!p.causal || kj <= qi);
+                const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -lse2)) : 0.f;
+                dsv[e] = pe * (dp[8 * kk + e] - delta);
+            }
+            dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
+                            Mfma<T>::pack2(dsv[4], dsv[5]), Mfma<T>::pack2(dsv[6], dsv[7])};
+        }
+        // dQ^T += K^T dS^T
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int db = 0; db < TL::DB; ++db)
+                dq[db] = Mfma<T>::mma(rd_cols<D>(sK[buf], db, kk, lane), dsf[kk], dq[db]);
+        if (t + 1 < nkt) commit(buf ^ 1);
+        __syncthreads();
+    }
+    if (qi < Nq) store_rowT<T, D>(static_cast<T*>(p.dq) + q_off + (int64_t)qi * d, dq, p.scale, d, h);
+}
+
+template <typename T, int D>
+hipError_t launch_typed(const BwdProblem& p, hipStream_t stream) {
+    constexpr int R = 32 * kWaves;
+    dim3 gk((p.seqlen_k + R - 1) / R, p.heads_kv, p.batch);
+    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D>), gk, dim3(kThreads), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.seqlen_q == 0) return e;   // no query rows: dK = dV = 0, no dQ
+    dim3 gq((p.seqlen_q + R - 1) / R, p.heads_q, p.batch);
+    hipLaunchKernelGGL((attn_bwd_dq_mfma_kernel<T, D>), gq, dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_dim(const BwdProblem& p, hipStream_t stream) {
+    if (p.head_dim <= 64) return launch_typed<T, 64>(p, stream);
+    return launch_typed<T, 128>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_attn_bwd_mfma(const BwdProblem& p, Dtype dt, hipStream_t stream) {
+    if (dt == Dtype::BF16) return launch_dim<bf16_t>(p, stream);
+    if (dt == Dtype::F16) return launch_dim<f16_t>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace aule

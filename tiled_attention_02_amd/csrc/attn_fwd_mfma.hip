@@ -44,20 +44,10 @@
 #include <cstdlib>
 
 #include "attn_device.h"
+#include "attn_mfma.h"
 
 namespace aule {
 namespace {
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 [[maybe_unused]] constexpr float kRescaleSlack = 8.0f; // log2 units
 [[maybe_unused]] constexpr float kSlackExp = 256.0f;   // 2^kRescaleSlack
@@ -68,44 +58,7 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 #define AULE_SOFTMAX_FAST 1
 #endif
 
-template <typename T> struct Mfma;
-template <> struct Mfma<bf16_t> {
-    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
-    // two fp32 -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32)
-    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
-    }
-    // acc + lo + hi of a packed pair, in fp32 (v_dot2 against (1, 1))
-    static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
-        const bf16x2 one = {(bf16_t)1.0f, (bf16_t)1.0f};
-        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), one, acc, false);
-    }
-};
-template <> struct Mfma<f16_t> {
-    static __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-    }
-    // two fp32 -> packed fp16 pair, round to nearest even (one v_cvt_pk_f16_f32)
-    static __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-        return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
-    }
-    static __device__ __forceinline__ float sum2(uint32_t pair, float acc) {
-        const f16x2 one = {(f16_t)1.0f, (f16_t)1.0f};
-        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), one, acc, false);
-    }
-};
-
-// sigma: swap bits 2 and 3 (an involution on 0..31)
-__device__ __forceinline__ int sigma(int m) {
-    return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
-}
-
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4;
 
 // 16-byte chunk swizzles (XOR on the chunk index inside a row).
 // K rows: the S^T reads of one instruction hit rows sigma(0..31) at one column; chunk c of

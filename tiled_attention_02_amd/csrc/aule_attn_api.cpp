@@ -58,6 +58,14 @@ aule_status_t check_common(int32_t head_dim, float scale, aule_dtype_t dtype) {
     return AULE_OK;
 }
 
+// fp16/bf16 backward on the matrix cores, fp32 (or AULE_FORCE_VALU=1) on the vector ALUs
+hipError_t launch_bwd(const aule::BwdProblem& p, aule_dtype_t dtype, hipStream_t stream) {
+    const aule::Dtype dt = static_cast<aule::Dtype>(dtype);
+    if (!force_valu() && (dt == aule::Dtype::F16 || dt == aule::Dtype::BF16))
+        return aule::launch_attn_bwd_mfma(p, dt, stream);
+    return aule::launch_attn_bwd(p, dt, stream);
+}
+
 aule_status_t dispatch(const aule::AttnProblem& p, aule_dtype_t dtype, hipStream_t stream) {
     aule::Dtype dt = static_cast<aule::Dtype>(dtype);
     hipError_t err;
@@ -330,7 +338,7 @@ aule_status_t aule_attn_bwd(const void* q, const void* k, const void* v, const v
         p.batch = batch; p.heads_q = heads_q; p.heads_kv = heads_kv; p.group = heads_q / heads_kv;
         p.seqlen_q = 0; p.seqlen_k = seqlen_k; p.head_dim = head_dim;
         p.scale = scale;
-        const hipError_t err = aule::launch_attn_bwd(p, static_cast<aule::Dtype>(dtype), stream);
+        const hipError_t err = launch_bwd(p, dtype, stream);
         if (err != hipSuccess)
             return fail(AULE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
         g_last_error[0] = '\0';
@@ -366,7 +374,7 @@ aule_status_t aule_attn_bwd(const void* q, const void* k, const void* v, const v
     p.seqlen_q = seqlen_q; p.seqlen_k = seqlen_k; p.head_dim = head_dim;
     p.causal = causal ? 1 : 0;
     p.scale = scale;
-    const hipError_t err = aule::launch_attn_bwd(p, static_cast<aule::Dtype>(dtype), stream);
+    const hipError_t err = launch_bwd(p, dtype, stream);
     if (err != hipSuccess)
         return fail(AULE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     g_last_error[0] = '\0';
