@@ -131,7 +131,14 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5, ln = lane & 31;
     const int Nq = p.seqlen_q, Nk = p.seqlen_k, d = p.head_dim, G = p.group;
-    const int j0 = blockIdx.x * 32 * kWaves, hk = blockIdx.y, b = blockIdx.z;
+    // flat grid, key blocks slowest: under causal masking block 0 walks every query tile and
+    // later blocks fewer, so the longest workgroups start first; the key blocks of one
+    // (batch, kv head) are heads_kv * batch apart, which keeps them on one XCD when that
+    // count is a multiple of 8 (they read the same Q and dO tiles)
+    const int per_kb = p.heads_kv * p.batch;
+    const int kb = blockIdx.x / per_kb, rem = blockIdx.x - kb * per_kb;
+    const int hk = rem % p.heads_kv, b = rem / p.heads_kv;
+    const int j0 = kb * 32 * kWaves;
     const int key = j0 + 32 * wave + ln;                 // this lane's key (B-operand column)
     const int64_t kv_off = ((int64_t)b * p.heads_kv + hk) * Nk * d;
     // work: (query head g of the group, 32-row query tile), causal from the first key on.
@@ -244,7 +251,14 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5, ln = lane & 31;
     const int Nq = p.seqlen_q, Nk = p.seqlen_k, d = p.head_dim;
-    const int i0 = blockIdx.x * 32 * kWaves, hq = blockIdx.y, b = blockIdx.z;
+    // flat grid, query blocks slowest and (causal) last block first: the longest walks start
+    // first
+    const int per_qb = p.heads_q * p.batch;
+    const int t_ = blockIdx.x / per_qb, rem = blockIdx.x - t_ * per_qb;
+    const int nqb = (Nq + 32 * kWaves - 1) / (32 * kWaves);
+    const int qblk = p.causal ? nqb - 1 - t_ : t_;
+    const int hq = rem % p.heads_q, b = rem / p.heads_q;
+    const int i0 = qblk * 32 * kWaves;
     const int hk = hq / p.group;
     const int qi = i0 + 32 * wave + ln;                  // this lane's query (B-operand column)
     const int64_t bh = (int64_t)b * p.heads_q + hq;
@@ -329,11 +343,14 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
 template <typename T, int D>
 hipError_t launch_typed(const BwdProblem& p, hipStream_t stream) {
     constexpr int R = 32 * kWaves;
-    dim3 gk((p.seqlen_k + R - 1) / R, p.heads_kv, p.batch);
+    const int64_t nk = (int64_t)((p.seqlen_k + R - 1) / R) * p.heads_kv * p.batch;
+    const int64_t nq = (int64_t)((p.seqlen_q + R - 1) / R) * p.heads_q * p.batch;
+    if (nk > INT32_MAX || nq > INT32_MAX) return hipErrorInvalidConfiguration;
+    dim3 gk((unsigned)nk);
     hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D>), gk, dim3(kThreads), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.seqlen_q == 0) return e;   // no query rows: dK = dV = 0, no dQ
-    dim3 gq((p.seqlen_q + R - 1) / R, p.heads_q, p.batch);
+    dim3 gq((unsigned)nq);
     hipLaunchKernelGGL((attn_bwd_dq_mfma_kernel<T, D>), gq, dim3(kThreads), 0, stream, p);
     return hipGetLastError();
 }
