@@ -44,6 +44,11 @@ BWD_SOURCES = ["tiled_attention_02_amd/csrc/attn_bwd_mfma.hip",
                "tiled_attention_02_amd/csrc/attn_mfma.h",
                "tiled_attention_02_amd/csrc/attn_device.h",
                "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
+SHORT_SOURCES = ["tiled_attention_02_amd/csrc/attn_fwd_short.hip",
+                 "tiled_attention_02_amd/csrc/attn_mfma.h",
+                 "tiled_attention_02_amd/csrc/attn_device.h",
+                 "tiled_attention_02_amd/csrc/attn_problem.h",
+                 "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -57,9 +62,11 @@ def kernel_source_hash(sources=KERNEL_SOURCES):
 
 
 def sources_for(workload):
-    from workloads import BWD_CONFIGS, DECODE_CONFIGS
+    from workloads import BWD_CONFIGS, DECODE_CONFIGS, SHORT_CONFIGS
     if workload in DECODE_CONFIGS:
         return DECODE_SOURCES
+    if workload in SHORT_CONFIGS:
+        return SHORT_SOURCES
     if workload in BWD_CONFIGS:
         return BWD_SOURCES
     return KERNEL_SOURCES
@@ -105,14 +112,14 @@ def parse():
 
 
 def device_inputs(cfg, torch):
-    from workloads import BwdConfig, DecodeConfig, DenseConfig
+    from workloads import BwdConfig, DecodeConfig, DenseConfig, ShortConfig
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[cfg.dtype]
     if isinstance(cfg, BwdConfig):
         q, k, v = cfg.inputs()
         do = cfg.grad()
         t = lambda x: torch.from_numpy(x).to(device="cuda", dtype=tdt)
         return (t(q), t(k), t(v), t(do)), (q, k, v, do)
-    if isinstance(cfg, (DenseConfig, DecodeConfig)):
+    if isinstance(cfg, (DenseConfig, DecodeConfig, ShortConfig)):
         q, k, v = cfg.inputs()
         t = lambda x: torch.from_numpy(x).to(device="cuda", dtype=tdt)
         return (t(q), t(k), t(v)), (q, k, v)
@@ -123,7 +130,7 @@ def device_inputs(cfg, torch):
 
 def make_step(cfg, dev_inputs, torch):
     import tiled_attention_02_amd as aule
-    from workloads import BwdConfig, DecodeConfig, DenseConfig
+    from workloads import BwdConfig, DecodeConfig, DenseConfig, ShortConfig
     if isinstance(cfg, BwdConfig):
         # O and the row LSE come from one forward before the timed region; a step is the
         # backward alone (both of its kernels)
@@ -142,7 +149,7 @@ def make_step(cfg, dev_inputs, torch):
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)   # outside the timed region
         return lambda: aule.flash_attention_decode(q, k, v, causal=cfg.causal,
                                                    scale=cfg.softmax_scale, out=out, workspace=ws)
-    if isinstance(cfg, DenseConfig):
+    if isinstance(cfg, (DenseConfig, ShortConfig)):
         q, k, v = dev_inputs
         out = torch.empty_like(q)
         return lambda: aule.flash_attention(q, k, v, causal=cfg.causal, scale=cfg.softmax_scale,
@@ -184,8 +191,22 @@ def cpu_baseline(cfg, host_inputs, budget_s):
     fit in about budget_s seconds; scaled to TFLOP/s with the same FLOP count."""
     import numpy as np
     import oracle
-    from workloads import BwdConfig, DecodeConfig, DenseConfig
+    from workloads import BwdConfig, DecodeConfig, DenseConfig, ShortConfig
     threads = len(os.sched_getaffinity(0))
+    if isinstance(cfg, ShortConfig):
+        # whole batch entries (every head) through the oracle, as many as fit the budget
+        q, k, v = host_inputs
+        t0 = time.perf_counter()
+        done = 0
+        while done < cfg.batch and time.perf_counter() - t0 <= budget_s:
+            b = done
+            oracle.attention_ref(q[b:b + 1], k[b:b + 1], v[b:b + 1], causal=cfg.causal,
+                                 scale=cfg.softmax_scale)
+            done += 1
+        dt = time.perf_counter() - t0
+        return {"value": cfg.flops() * done / cfg.batch / dt / 1e12, "unit": "TFLOP/s",
+                "cores": threads, "kind": "oracle",
+                "sample": f"{done} of {cfg.batch} batch entries (all heads), {dt:.1f} s"}
     if isinstance(cfg, BwdConfig):
         # whole (batch, query head) slices: the oracle's gradients of one query head against
         # its kv head, 10*d FLOP per unmasked pair like the GPU figure
@@ -296,9 +317,9 @@ def main():
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import torch
-    from workloads import (BWD_CONFIGS, CONFIGS, DECODE_CONFIGS, MODS_CONFIGS, BwdConfig,
-                           DecodeConfig, ModsConfig)
-    ALL = {**CONFIGS, **DECODE_CONFIGS, **BWD_CONFIGS, **MODS_CONFIGS}
+    from workloads import (BWD_CONFIGS, CONFIGS, DECODE_CONFIGS, MODS_CONFIGS, SHORT_CONFIGS,
+                           BwdConfig, DecodeConfig, ModsConfig, ShortConfig)
+    ALL = {**CONFIGS, **DECODE_CONFIGS, **BWD_CONFIGS, **MODS_CONFIGS, **SHORT_CONFIGS}
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
@@ -353,6 +374,12 @@ def main():
         line["config"]["pct_of_peak"] = round(100 * line["value"] / HBM_PEAK_GBS, 2)
         line["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    if isinstance(cfg, ShortConfig):
+        # 35 FLOP per compulsory byte, far left of the ridge: the HBM roofline bounds it
+        gbs = cfg.bytes_compulsory() / kern_s / 1e9
+        line["config"]["gbs_compulsory"] = round(cfg.bytes_compulsory() / wall_s / 1e9, 1)
+        line["roofline"].update({"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)})
     if args.all:
         for name, c in ALL.items():
             if name == cfg.name:
@@ -372,7 +399,11 @@ def main():
 
 
 def describe(cfg):
-    from workloads import BwdConfig, DecodeConfig, DenseConfig
+    from workloads import BwdConfig, DecodeConfig, DenseConfig, ShortConfig
+    if isinstance(cfg, ShortConfig):
+        return (f"{cfg.dtype} short {'causal' if cfg.causal else 'non-causal'} B={cfg.batch} "
+                f"Hq={cfg.heads_q} Hkv={cfg.heads_kv} Nq={cfg.seqlen_q} Nk={cfg.seqlen_k} "
+                f"d={cfg.head_dim} scale={cfg.softmax_scale:.6g}")
     if isinstance(cfg, BwdConfig):
         return (f"{cfg.dtype} backward {'causal' if cfg.causal else 'non-causal'} B={cfg.batch} "
                 f"Hq={cfg.heads_q} Hkv={cfg.heads_kv} N={cfg.seqlen} d={cfg.head_dim} "

@@ -1,6 +1,7 @@
 // gfx950 matrix-core helpers shared by the forward and backward kernels: operand vector
-// types, the 32x32x16 bf16/fp16 MFMA with its pack / dot helpers, and the row permutation
-// sigma that makes a product's accumulator registers the operand of the next product.
+// types, the 32x32x16 bf16/fp16 MFMA with its pack / dot helpers, the row permutation
+// sigma that makes a product's accumulator registers the operand of the next product, and
+// the K/V tile swizzles and global -> LDS copy of the forward kernels.
 //
 // v_mfma_f32_32x32x16_{bf16,f16} lane layouts (lane l, half h = l / 32):
 //   A (32 x 16): lane l holds row l % 32, k = 8h .. 8h + 7 (one u32x4 of 8 elements)
@@ -72,5 +73,48 @@ template <> struct Mfma<f16_t> {
 __device__ __forceinline__ int sigma(int m) {
     return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte chunk swizzles (XOR on the chunk index inside a row) of K and V tiles in LDS.
+// K rows: the S^T reads of one instruction hit rows sigma(0..31) at one column; chunk c of
+//   row r sits at c ^ (sigma(r % 32) % KC), so those reads spread over distinct chunks.
+// V rows: a transposed read touches 4 consecutive rows x 2 (or 4) neighbouring chunks; the
+//   per-row XOR masks below make those slots distinct modulo 8 and modulo 16 chunks.
+template <int KC> __device__ __forceinline__ int kswz(int row) { return sigma(row & 31) & (KC - 1); }
+template <int KC> __device__ __forceinline__ int vswz(int row) {
+    if constexpr (KC == 16) return (0xCA60 >> (4 * (row & 3))) & 15;   // 0, 6, 10, 12
+    else return 2 * (row & 3);
+}
+
+[[maybe_unused]] constexpr uint32_t kBufferFlags = 0x00020000u;   // raw buffer, 32-bit data format
+[[maybe_unused]] constexpr uint32_t kOobOffset = 0x7FFFFFF0u;     // an offset past any slice: reads as zero
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// One 16-byte global -> LDS copy per lane: LDS[m0 + 16 * lane] = buffer[voffset], zero when
+// voffset lies past the descriptor's size. Written as inline asm so the compiler does not
+// track it: its alias analysis cannot tell the destination buffer from the buffers being
+// read and would otherwise wait for every copy right after issuing it. Completion is
+// ordered explicitly instead (s_waitcnt vmcnt, plus s_barrier when other waves read the
+// data). M0 is saved and restored around the copy.
+__device__ __forceinline__ void lds_copy16(i32x4 rsrc, uint32_t voffset, uint32_t lds_addr) {
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(voffset), "s"(rsrc), "s"(lds_addr));
+}
+
+// Raw buffer descriptor (stride 0, bounds-checked by num_records bytes).
+__device__ __forceinline__ i32x4 buffer_desc(const void* base, int num_records) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)b, (int)((uint32_t)(b >> 32) & 0xFFFFu), num_records, (int)kBufferFlags};
+}
+#endif  // __HIP_DEVICE_COMPILE__
 
 }  // namespace aule

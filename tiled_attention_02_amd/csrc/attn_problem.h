@@ -55,5 +55,9 @@ hipError_t launch_attn_fwd_valu(const AttnProblem& p, Dtype dt, hipStream_t stre
 hipError_t launch_attn_fwd_mfma(const AttnProblem& p, Dtype dt, hipStream_t stream);
 // True when the MFMA path handles this problem (fp16/bf16 and a supported head_dim).
 bool mfma_supports(const AttnProblem& p, Dtype dt);
+// Short sequences (dense fp16/bf16, at most 128 keys, at most 16 (query head, 32-row block)
+// items per kv head): the whole K/V slice in LDS, one workgroup per (batch, kv head).
+hipError_t launch_attn_fwd_short(const AttnProblem& p, Dtype dt, hipStream_t stream);
+bool short_supports(const AttnProblem& p, Dtype dt);
 
 }  // namespace aule

@@ -69,7 +69,9 @@ hipError_t launch_bwd(const aule::BwdProblem& p, aule_dtype_t dtype, hipStream_t
 aule_status_t dispatch(const aule::AttnProblem& p, aule_dtype_t dtype, hipStream_t stream) {
     aule::Dtype dt = static_cast<aule::Dtype>(dtype);
     hipError_t err;
-    if (!force_valu() && aule::mfma_supports(p, dt))
+    if (!force_valu() && aule::short_supports(p, dt))
+        err = aule::launch_attn_fwd_short(p, dt, stream);
+    else if (!force_valu() && aule::mfma_supports(p, dt))
         err = aule::launch_attn_fwd_mfma(p, dt, stream);
     else
         err = aule::launch_attn_fwd_valu(p, dt, stream);

@@ -259,6 +259,46 @@ class DecodeConfig:
 
 
 @dataclass(frozen=True)
+class ShortConfig:
+    """Short queries against short keys at a large batch (cross-attention of a diffusion
+    model): Nq and Nk at most 128, so each (batch, kv head) fits the short-sequence kernel."""
+    name: str
+    dtype: str
+    batch: int
+    heads_q: int
+    heads_kv: int
+    seqlen_q: int
+    seqlen_k: int
+    head_dim: int
+    causal: bool
+    seed: int
+    sigma: float = 1.0
+    scale: float | None = None
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+
+    def pairs(self) -> int:
+        nq, nk = self.seqlen_q, self.seqlen_k
+        per = nq * (nq + 1) // 2 if self.causal else nq * nk
+        return self.batch * per
+
+    def flops(self) -> int:
+        return 4 * self.head_dim * self.heads_q * self.pairs()
+
+    def bytes_compulsory(self) -> int:
+        """Q read and O written once, K and V read once."""
+        e = {"f32": 4, "f16": 2, "bf16": 2}[self.dtype]
+        d, B = self.head_dim, self.batch
+        return e * d * B * (2 * self.heads_q * self.seqlen_q + 2 * self.heads_kv * self.seqlen_k)
+
+    def inputs(self):
+        return dense_inputs(self.batch, self.heads_q, self.heads_kv, self.seqlen_q, self.seqlen_k,
+                            self.head_dim, seed=self.seed, sigma=self.sigma, dtype=self.dtype)
+
+
+@dataclass(frozen=True)
 class BwdConfig(DenseConfig):
     """The backward of a dense workload: dQ, dK, dV from Q, K, V, O, dO and the row LSE."""
 
@@ -316,4 +356,11 @@ MODS_CONFIGS = {
     "m1_bf16_varlen_mods": ModsConfig("m1_bf16_varlen_mods", "bf16", 16, 64, 4096, 16, 128, True,
                                       seed=3, window_left=1024, window_right=0, softcap=50.0,
                                       alibi=True),
+}
+
+# Short-sequence cross-attention (the diffusion-model shape of 64 queries against 77 keys,
+# 768 = 12 heads x 64 channels), non-causal, at a batch of 256 so the launch fills the GPU.
+SHORT_CONFIGS = {
+    "s1_bf16_short_cross": ShortConfig("s1_bf16_short_cross", "bf16", 256, 12, 12, 64, 77, 64,
+                                       False, seed=7),
 }
