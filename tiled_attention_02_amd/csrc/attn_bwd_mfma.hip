@@ -33,35 +33,35 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLog2eF = 1.4426950408889634f;
 
-template <int D>
+template <int D, int NT = kThreads>
 struct Tile {
     static constexpr int RS = D * 2 + 16;                 // bytes per LDS row
     static constexpr int CPR = D / 8;                     // 16-byte chunks per row
     static constexpr int BYTES = 32 * RS;
-    static constexpr int NCH = 32 * CPR / kThreads;       // chunks per thread per tile
+    static constexpr int NCH = 32 * CPR / NT;             // chunks per thread per tile
     static constexpr int KS = D / 16;                     // k-steps over head_dim
     static constexpr int DB = D / 32;                     // 32-row blocks of head_dim
-    static_assert(NCH >= 1 && NCH * kThreads == 32 * CPR, "tile chunks must split evenly");
+    static_assert(NCH >= 1 && NCH * NT == 32 * CPR, "tile chunks must split evenly");
 };
 
 // Rows [r0, r0 + 32) of a [rows, d] slice as 16-byte chunks, this thread's share (zero past
 // the last row and past head_dim).
-template <typename T, int D>
-__device__ __forceinline__ void fetch_rows(u32x4 (&c)[Tile<D>::NCH], const T* base, int r0, int rows, int d) {
+template <typename T, int D, int NT = kThreads>
+__device__ __forceinline__ void fetch_rows(u32x4 (&c)[(Tile<D, NT>::NCH)], const T* base, int r0, int rows, int d) {
 #pragma unroll
-    for (int i = 0; i < Tile<D>::NCH; ++i) {
-        const int idx = (int)threadIdx.x + kThreads * i;
+    for (int i = 0; i < Tile<D, NT>::NCH; ++i) {
+        const int idx = (int)threadIdx.x + NT * i;
         const int row = idx / Tile<D>::CPR, ch = idx % Tile<D>::CPR;
         const int r = r0 + row;
         c[i] = (r < rows && ch * 8 < d) ? *reinterpret_cast<const u32x4*>(base + (int64_t)r * d + ch * 8)
                                         : u32x4{0u, 0u, 0u, 0u};
     }
 }
-template <int D>
-__device__ __forceinline__ void put_rows(char* tile, const u32x4 (&c)[Tile<D>::NCH]) {
+template <int D, int NT = kThreads>
+__device__ __forceinline__ void put_rows(char* tile, const u32x4 (&c)[(Tile<D, NT>::NCH)]) {
 #pragma unroll
-    for (int i = 0; i < Tile<D>::NCH; ++i) {
-        const int idx = (int)threadIdx.x + kThreads * i;
+    for (int i = 0; i < Tile<D, NT>::NCH; ++i) {
+        const int idx = (int)threadIdx.x + NT * i;
         *reinterpret_cast<u32x4*>(tile + (idx / Tile<D>::CPR) * Tile<D>::RS + (idx % Tile<D>::CPR) * 16) = c[i];
     }
 }
@@ -118,10 +118,16 @@ __device__ __forceinline__ void store_rowT(T* row, const f32x16 (&acc)[Tile<D>::
         }
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+// PASS 0 accumulates dV only (S and dV^T += dO^T P: no V, O or D needed), PASS 1 dK only
+// (S, dP and dK^T += Q^T dS). One gradient per pass halves the accumulators, so each pass
+// fits two waves per SIMD, whose matrix products then overlap the other wave's
+// exponentials; the price is S computed twice. WV waves own 32 keys each: the Q / dO / O
+// rows of the group are read once per 32 * WV keys, so wider workgroups cut that traffic.
+template <typename T, int D, int PASS, int WV>
+__global__ __launch_bounds__(WV * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
-    using TL = Tile<D>;
+    constexpr int NT = WV * 64;
+    using TL = Tile<D, NT>;
     __shared__ __attribute__((aligned(16))) char sQ[2][TL::BYTES];
     __shared__ __attribute__((aligned(16))) char sdO[2][TL::BYTES];
     __shared__ __attribute__((aligned(16))) float sL[2][32];
@@ -138,7 +144,7 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     const int per_kb = p.heads_kv * p.batch;
     const int kb = blockIdx.x / per_kb, rem = blockIdx.x - kb * per_kb;
     const int hk = rem % p.heads_kv, b = rem / p.heads_kv;
-    const int j0 = kb * 32 * kWaves;
+    const int j0 = kb * 32 * WV;
     const int key = j0 + 32 * wave + ln;                 // this lane's key (B-operand column)
     const int64_t kv_off = ((int64_t)b * p.heads_kv + hk) * Nk * d;
     // work: (query head g of the group, 32-row query tile), causal from the first key on.
@@ -148,63 +154,67 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     const int ntile = Nq > i_start ? (Nq - i_start + 31) / 32 : 0;
     const int nit = G * ntile;
 
-    u32x4 kf[TL::KS], vf[TL::KS];
+    u32x4 kf[TL::KS], vf[PASS == 1 ? TL::KS : 1];
     if (nit > 0) {
         fetch_operand<T, D>(kf, static_cast<const T*>(p.k) + kv_off, key, Nk, d, h);
-        fetch_operand<T, D>(vf, static_cast<const T*>(p.v) + kv_off, key, Nk, d, h);
+        if constexpr (PASS == 1) fetch_operand<T, D>(vf, static_cast<const T*>(p.v) + kv_off, key, Nk, d, h);
     }
 
-    f32x16 dk[TL::DB], dv[TL::DB];
+    f32x16 acc[TL::DB];   // dV^T (PASS 0) or dK^T (PASS 1)
 #pragma unroll
-    for (int db = 0; db < TL::DB; ++db) { dk[db] = f32x16{}; dv[db] = f32x16{}; }
+    for (int db = 0; db < TL::DB; ++db) acc[db] = f32x16{};
     const float c2 = p.scale * kLog2eF;
 
-    u32x4 cq[TL::NCH], cdo[TL::NCH], co[TL::NCH];
-    float lse_v = 0.f;
-    auto fetch = [&](int it) {
+    // Register staging of one query tile's global loads. Two sets: tile it + 2 is fetched
+    // into the set that held tile it while tile it + 1 (fetched an iteration earlier) is
+    // committed to LDS, so each load has two iterations to arrive.
+    struct Stage {
+        u32x4 q[TL::NCH], dO[TL::NCH], o[PASS == 1 ? TL::NCH : 1];
+        float lse;
+    };
+    auto fetch = [&](int it, Stage& st) {
         const int g = it / ntile, i0 = i_start + 32 * (it - g * ntile);
         const int64_t bh = (int64_t)b * p.heads_q + hk * G + g;
         const int64_t q_off = bh * Nq * d;
-        fetch_rows<T, D>(cq, static_cast<const T*>(p.q) + q_off, i0, Nq, d);
-        fetch_rows<T, D>(cdo, static_cast<const T*>(p.do_) + q_off, i0, Nq, d);
-        fetch_rows<T, D>(co, static_cast<const T*>(p.o) + q_off, i0, Nq, d);
+        fetch_rows<T, D, NT>(st.q, static_cast<const T*>(p.q) + q_off, i0, Nq, d);
+        fetch_rows<T, D, NT>(st.dO, static_cast<const T*>(p.do_) + q_off, i0, Nq, d);
+        if constexpr (PASS == 1) fetch_rows<T, D, NT>(st.o, static_cast<const T*>(p.o) + q_off, i0, Nq, d);
         const int r = i0 + (int)threadIdx.x;
-        lse_v = (threadIdx.x < 32 && r < Nq) ? p.lse[bh * Nq + r] : 0.f;
+        st.lse = (threadIdx.x < 32 && r < Nq) ? p.lse[bh * Nq + r] : 0.f;
     };
-    auto commit = [&](int buf) {
-        put_rows<D>(sQ[buf], cq);
-        put_rows<D>(sdO[buf], cdo);
+    auto commit = [&](int buf, const Stage& st) {
+        put_rows<D, NT>(sQ[buf], st.q);
+        put_rows<D, NT>(sdO[buf], st.dO);
         // D_i = do_i . o_i: a chunk pair per thread, summed over the CPR chunks of a row
         // (consecutive lanes)
+        if constexpr (PASS == 1)
 #pragma unroll
         for (int i = 0; i < TL::NCH; ++i) {
             float x = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) x = Mfma<T>::dot2(cdo[i][w], co[i][w], x);
+            for (int w = 0; w < 4; ++w) x = Mfma<T>::dot2(st.dO[i][w], st.o[i][w], x);
 #pragma unroll
             for (int off = 1; off < TL::CPR; off <<= 1) x += __shfl_xor(x, off);
-            const int idx = (int)threadIdx.x + kThreads * i;
+            const int idx = (int)threadIdx.x + NT * i;
             if (idx % TL::CPR == 0) sD[buf][idx / TL::CPR] = x;
         }
-        if (threadIdx.x < 32) sL[buf][threadIdx.x] = lse_v * kLog2eF;
+        if (threadIdx.x < 32) sL[buf][threadIdx.x] = st.lse * kLog2eF;
     };
 
-    if (nit > 0) {
-        fetch(0);
-        commit(0);
-    }
-    __syncthreads();
-    for (int it = 0; it < nit; ++it) {
+    const int kw0 = j0 + 32 * wave;   // this wave's first key
+    auto body = [&](int it, Stage& mine, const Stage& other) {
         const int buf = it & 1;
         const int g = it / ntile, i0 = i_start + 32 * (it - g * ntile);
-        if (it + 1 < nit) fetch(it + 1);
+        if (it + 2 < nit) fetch(it + 2, mine);
         // S = Q K^T, dP = dO V^T: register r holds query i0 + 16(r/8) + 8h + r%8, key `key`
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < TL::KS; ++ks) {
             s = Mfma<T>::mma(rd_rows<D>(sQ[buf], ks, lane), kf[ks], s);
-            dp = Mfma<T>::mma(rd_rows<D>(sdO[buf], ks, lane), vf[ks], dp);
+            if constexpr (PASS == 1) dp = Mfma<T>::mma(rd_rows<D>(sdO[buf], ks, lane), vf[ks], dp);
         }
+        // tiles away from the diagonal and the ends need no mask (a uniform branch)
+        const bool inner = i0 + 32 <= Nq && kw0 + 32 <= Nk && (!p.causal || kw0 + 31 <= i0);
         u32x4 pf[2], dsf[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -213,30 +223,44 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int qi = i0 + q0 + e;
-                const bool vis = qi < Nq && key < Nk && (!p.causal || key <= qi);
+                const bool vis = inner || (qi < Nq && key < Nk && (!p.causal || key <= qi));
                 const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -sL[buf][q0 + e])) : 0.f;
                 pv[e] = pe;
-                dsv[e] = pe * (dp[8 * kk + e] - sD[buf][q0 + e]);
+                dsv[e] = PASS == 1 ? pe * (dp[8 * kk + e] - sD[buf][q0 + e]) : 0.f;
             }
-            pf[kk] = u32x4{Mfma<T>::pack2(pv[0], pv[1]), Mfma<T>::pack2(pv[2], pv[3]),
-                           Mfma<T>::pack2(pv[4], pv[5]), Mfma<T>::pack2(pv[6], pv[7])};
-            dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
+            if constexpr (PASS == 0)
+                pf[kk] = u32x4{Mfma<T>::pack2(pv[0], pv[1]), Mfma<T>::pack2(pv[2], pv[3]),
+                               Mfma<T>::pack2(pv[4], pv[5]), Mfma<T>::pack2(pv[6], pv[7])};
+            else
+                dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
                             Mfma<T>::pack2(dsv[4], dsv[5]), Mfma<T>::pack2(dsv[6], dsv[7])};
         }
-        // dV^T += dO^T P, dK^T += Q^T dS
+        // dV^T += dO^T P (PASS 0) or dK^T += Q^T dS (PASS 1)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int db = 0; db < TL::DB; ++db) {
-                dv[db] = Mfma<T>::mma(rd_cols<D>(sdO[buf], db, kk, lane), pf[kk], dv[db]);
-                dk[db] = Mfma<T>::mma(rd_cols<D>(sQ[buf], db, kk, lane), dsf[kk], dk[db]);
+                if constexpr (PASS == 0) acc[db] = Mfma<T>::mma(rd_cols<D>(sdO[buf], db, kk, lane), pf[kk], acc[db]);
+                else acc[db] = Mfma<T>::mma(rd_cols<D>(sQ[buf], db, kk, lane), dsf[kk], acc[db]);
             }
-        if (it + 1 < nit) commit(buf ^ 1);
+        if (it + 1 < nit) commit(buf ^ 1, other);
         __syncthreads();
+    };
+
+    Stage st0, st1;
+    if (nit > 0) {
+        fetch(0, st0);
+        commit(0, st0);
+    }
+    if (nit > 1) fetch(1, st1);
+    __syncthreads();
+    for (int it = 0; it < nit; it += 2) {
+        body(it, st0, st1);
+        if (it + 1 < nit) body(it + 1, st1, st0);
     }
     if (key < Nk) {
-        store_rowT<T, D>(static_cast<T*>(p.dk) + kv_off + (int64_t)key * d, dk, p.scale, d, h);
-        store_rowT<T, D>(static_cast<T*>(p.dv) + kv_off + (int64_t)key * d, dv, 1.f, d, h);
+        if constexpr (PASS == 1) store_rowT<T, D>(static_cast<T*>(p.dk) + kv_off + (int64_t)key * d, acc, p.scale, d, h);
+        else store_rowT<T, D>(static_cast<T*>(p.dv) + kv_off + (int64_t)key * d, acc, 1.f, d, h);
     }
 }
 
@@ -252,12 +276,16 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
     const int h = lane >> 5, ln = lane & 31;
     const int Nq = p.seqlen_q, Nk = p.seqlen_k, d = p.head_dim;
     // flat grid, query blocks slowest and (causal) last block first: the longest walks start
-    // first
+    // first. Within a block index the G query heads of one (batch, kv head) are
+    // batch * heads_kv apart, which puts them on one XCD (sharing its L2 copy of that K/V)
+    // when that count is a multiple of 8.
     const int per_qb = p.heads_q * p.batch;
     const int t_ = blockIdx.x / per_qb, rem = blockIdx.x - t_ * per_qb;
     const int nqb = (Nq + 32 * kWaves - 1) / (32 * kWaves);
     const int qblk = p.causal ? nqb - 1 - t_ : t_;
-    const int hq = rem % p.heads_q, b = rem / p.heads_q;
+    const int nkvu = p.batch * p.heads_kv;
+    const int gi = rem / nkvu, u = rem - gi * nkvu;
+    const int b = u / p.heads_kv, hq = (u - b * p.heads_kv) * p.group + gi;
     const int i0 = qblk * 32 * kWaves;
     const int hk = hq / p.group;
     const int qi = i0 + 32 * wave + ln;                  // this lane's query (B-operand column)
@@ -290,23 +318,21 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
 
     const int j_end = p.causal ? min(Nk, i0 + 32 * kWaves) : Nk;
     const int nkt = (j_end + 31) / 32;
-    u32x4 ck[TL::NCH], cv[TL::NCH];
-    auto fetch = [&](int t) {
-        fetch_rows<T, D>(ck, Kb, 32 * t, Nk, d);
-        fetch_rows<T, D>(cv, Vb, 32 * t, Nk, d);
+    // two register staging sets, as in the dK / dV kernel: key tile t + 2 is fetched while
+    // tile t + 1 (fetched an iteration earlier) is committed to LDS
+    struct Stage { u32x4 k[TL::NCH], v[TL::NCH]; };
+    auto fetch = [&](int t, Stage& st) {
+        fetch_rows<T, D>(st.k, Kb, 32 * t, Nk, d);
+        fetch_rows<T, D>(st.v, Vb, 32 * t, Nk, d);
     };
-    auto commit = [&](int buf) {
-        put_rows<D>(sK[buf], ck);
-        put_rows<D>(sV[buf], cv);
+    auto commit = [&](int buf, const Stage& st) {
+        put_rows<D>(sK[buf], st.k);
+        put_rows<D>(sV[buf], st.v);
     };
-    if (nkt > 0) {
-        fetch(0);
-        commit(0);
-    }
-    __syncthreads();
-    for (int t = 0; t < nkt; ++t) {
+    const int qw0 = i0 + 32 * wave;   // this wave's first query row
+    auto body = [&](int t, Stage& mine, const Stage& other) {
         const int buf = t & 1;
-        if (t + 1 < nkt) fetch(t + 1);
+        if (t + 2 < nkt) fetch(t + 2, mine);
         // S^T = K Q^T, dP^T = V dO^T: register r holds key 32t + 16(r/8) + 8h + r%8, query qi
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
@@ -314,6 +340,8 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
             s = Mfma<T>::mma(rd_rows<D>(sK[buf], ks, lane), qf[ks], s);
             dp = Mfma<T>::mma(rd_rows<D>(sV[buf], ks, lane), dof[ks], dp);
         }
+        // key tiles before the diagonal and away from the ends need no mask (uniform)
+        const bool inner = qw0 + 32 <= Nq && 32 * t + 32 <= Nk && (!p.causal || 32 * t + 31 <= qw0);
         u32x4 dsf[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -321,7 +349,7 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int kj = 32 * t + 16 * kk + 8 * h + e;
-                const bool vis = qi < Nq && kj < Nk && (!p.causal || kj <= qi);
+                const bool vis = inner || (qi < Nq && kj < Nk && (!p.causal || kj <= qi));
                 const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -lse2)) : 0.f;
                 dsv[e] = pe * (dp[8 * kk + e] - delta);
             }
@@ -334,8 +362,19 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
 #pragma unroll
             for (int db = 0; db < TL::DB; ++db)
                 dq[db] = Mfma<T>::mma(rd_cols<D>(sK[buf], db, kk, lane), dsf[kk], dq[db]);
-        if (t + 1 < nkt) commit(buf ^ 1);
+        if (t + 1 < nkt) commit(buf ^ 1, other);
         __syncthreads();
+    };
+    Stage st0, st1;
+    if (nkt > 0) {
+        fetch(0, st0);
+        commit(0, st0);
+    }
+    if (nkt > 1) fetch(1, st1);
+    __syncthreads();
+    for (int t = 0; t < nkt; t += 2) {
+        body(t, st0, st1);
+        if (t + 1 < nkt) body(t + 1, st1, st0);
     }
     if (qi < Nq) store_rowT<T, D>(static_cast<T*>(p.dq) + q_off + (int64_t)qi * d, dq, p.scale, d, h);
 }
@@ -343,12 +382,19 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
 template <typename T, int D>
 hipError_t launch_typed(const BwdProblem& p, hipStream_t stream) {
     constexpr int R = 32 * kWaves;
-    const int64_t nk = (int64_t)((p.seqlen_k + R - 1) / R) * p.heads_kv * p.batch;
+    // 256 keys per dK / dV workgroup at head_dim 128 (a 32-row tile of 16-byte chunks then
+    // splits evenly over 512 threads), 128 at 64
+    constexpr int WV = D == 128 ? 8 : 4;
+    constexpr int RK = 32 * WV;
+    const int64_t nk = (int64_t)((p.seqlen_k + RK - 1) / RK) * p.heads_kv * p.batch;
     const int64_t nq = (int64_t)((p.seqlen_q + R - 1) / R) * p.heads_q * p.batch;
     if (nk > INT32_MAX || nq > INT32_MAX) return hipErrorInvalidConfiguration;
     dim3 gk((unsigned)nk);
-    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D>), gk, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 0, WV>), gk, dim3(WV * 64), 0, stream, p);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 1, WV>), gk, dim3(WV * 64), 0, stream, p);
+    e = hipGetLastError();
     if (e != hipSuccess || p.seqlen_q == 0) return e;   // no query rows: dK = dV = 0, no dQ
     dim3 gq((unsigned)nq);
     hipLaunchKernelGGL((attn_bwd_dq_mfma_kernel<T, D>), gq, dim3(kThreads), 0, stream, p);
