@@ -191,6 +191,20 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     };
     const int ngroups = p.heads_q / GH;
     const int NG = p.batch * ngroups;
+    // Varlen grid (virtual tile, head group): workgroups go to the 8 XCDs round-robin in
+    // dispatch order (x fastest), so neighbouring tiles of one (sequence, head) would land
+    // on different XCDs and each XCD's L2 would fetch that K/V again. When the head-group
+    // count divides by 8 the linear block id is remapped (a bijection) so that every tile of
+    // a head group runs on one XCD: XCD = group % 8, tiles in order within it.
+    int vx = blockIdx.x, vy = blockIdx.y;
+    if constexpr (VARLEN) {
+        if ((gridDim.y & 7) == 0) {
+            const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+            const int xcd = lin & 7, slot = lin >> 3, per = gridDim.y >> 3;
+            vx = slot / per;
+            vy = xcd + 8 * (slot - vx * per);
+        }
+    }
     auto make_item = [&](int x, Item& it) -> bool {
         int bidx, hq0, tile, Lq, Lk;
         int64_t tok0 = 0;
@@ -198,7 +212,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
             TileSlot s = locate_varlen_tile(p.cu_seqlens, p.batch, p.total_tokens, BMW, x, CAUSAL);
             if (!s.valid) return false;
             bidx = s.seq; tok0 = s.tok0; tile = s.tile; Lq = s.len_q; Lk = s.len_k;
-            hq0 = blockIdx.y * GH;
+            hq0 = vy * GH;
         } else {
             // groups = (batch, GH query heads sharing one kv head). Item x runs on XCD x % 8
             // (workgroup x does, and a persistent workgroup only takes items of its own XCD);
@@ -271,7 +285,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     };
 
     Item cur;
-    if (!make_item(PERSIST ? item_x(0) : (int)blockIdx.x, cur)) return;
+    if (!make_item(PERSIST ? item_x(0) : vx, cur)) return;
 
     // ---------------------------------------------------------------- Q -> registers
     // Issued after the first K/V tile copy so that both latencies overlap; a negative scale
