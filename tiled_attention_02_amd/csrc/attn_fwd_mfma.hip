@@ -217,14 +217,19 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
             // groups = (batch, GH query heads sharing one kv head). Item x runs on XCD x % 8
             // (workgroup x does, and a persistent workgroup only takes items of its own XCD);
             // when the groups split evenly, each XCD gets whole groups so that their K/V stay
-            // in that XCD's L2. Within an XCD (or the whole grid) the longest causal tiles
-            // come first.
+            // in that XCD's L2. The longest causal tiles come first (within each group of an
+            // XCD, or over the whole grid).
             if (x >= n_qtiles * NG) return false;
             int t, g;
             if (NG % 8 == 0) {
+                // group-major within an XCD: all q-tiles of one group (longest first), then
+                // the next group, so one group's K/V is live in the XCD's L2 at a time (the
+                // snake order of the persistent workgroups keeps each one's causal work
+                // equal over every two rounds of a group)
                 const int per = NG / 8, xcd = x & 7, l = x >> 3;
-                t = l / per;
-                g = xcd * per + (l - t * per);
+                const int gl = l / n_qtiles;
+                t = l - gl * n_qtiles;
+                g = xcd * per + gl;
             } else {
                 t = x / NG;
                 g = x - t * NG;
