@@ -198,6 +198,28 @@ def test_batch_and_longer_dense():
     check_dense(2, 4, 1, 700, 900, 128, "bf16", False, seed=23)
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_xcd_group_major_dense(causal):
+    """(batch, query-head group) counts that divide by 8 take the XCD-local, group-major item
+    order of the persistent kernel: B=2 x (16 heads / 4 per group) = 8 groups, and 16 groups."""
+    check_dense(2, 16, 4, 700, 700, 128, "bf16", causal, seed=24)
+    check_dense(4, 16, 4, 333, 333, 128, "f16", causal, seed=25)
+
+
+@pytest.mark.parametrize("H", [8, 24])
+@pytest.mark.parametrize("causal", [True, False])
+def test_varlen_xcd_remap(H, causal):
+    """Head counts that divide by 8 take the remapped (tile, head) varlen grid."""
+    lengths = [300, 1, 0, 129, 700, 64]
+    d = 128
+    say(f"varlen remap H={H} causal={causal}")
+    qkv, cu = varlen_inputs(lengths, H, d, seed=40 + H, dtype="bf16")
+    got = run_varlen(qkv, cu, "bf16", causal, 1 / math.sqrt(d))
+    ref = oracle.attention_ref_varlen(qkv, cu, causal=causal, scale=1 / math.sqrt(d))
+    assert np.all(np.isfinite(got))
+    assert np.max(np.abs(got - ref)) <= TOL["bf16"]
+
+
 # ------------------------------------------------------------------ varlen edges
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
