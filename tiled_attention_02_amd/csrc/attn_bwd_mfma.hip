@@ -35,9 +35,11 @@ constexpr float kLog2eF = 1.4426950408889634f;
 
 template <int D, int NT = kThreads>
 struct Tile {
-    static constexpr int RS = D * 2 + 16;                 // bytes per LDS row
+    static constexpr int RS = D * 2;                      // bytes per LDS row (swizzled layouts)
+    static constexpr int RSP = D * 2 + 16;                // bytes per LDS row (PAD layout)
     static constexpr int CPR = D / 8;                     // 16-byte chunks per row
     static constexpr int BYTES = 32 * RS;
+    static constexpr int BYTESP = 32 * RSP;
     static constexpr int NCH = 32 * CPR / NT;             // chunks per thread per tile
     static constexpr int KS = D / 16;                     // k-steps over head_dim
     static constexpr int DB = D / 32;                     // 32-row blocks of head_dim
@@ -57,31 +59,52 @@ __device__ __forceinline__ void fetch_rows(u32x4 (&c)[(Tile<D, NT>::NCH)], const
                                         : u32x4{0u, 0u, 0u, 0u};
     }
 }
-template <int D, int NT = kThreads>
+// Two LDS layouts of a 32-row tile, one per read pattern, with the XOR swizzles of the
+// forward kernel's K and V tiles (chunk c of row r stored at chunk c ^ swz(r)):
+//   ROWS: rd_rows reads one chunk of rows sigma(0..31) per instruction -> kswz;
+//   COLS: rd_cols reads 4 consecutive rows x 2 neighbouring chunks per 16 lanes -> vswz.
+// A tile read both ways is stored twice. PAD: unswizzled rows padded by 16 bytes, read both
+// ways from one copy (the transposed reads then conflict 2-way; the dQ kernel keeps it, where
+// a second copy of K cost more than the conflicts).
+enum Layout { ROWS = 0, COLS = 1, PAD = 2 };
+template <int D, int L>
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (L == ROWS) return kswz<D / 8>(row);
+    else if constexpr (L == COLS) return vswz<D / 8>(row);
+    else return 0;
+}
+template <int D, int L> constexpr int row_bytes() { return L == PAD ? Tile<D>::RSP : Tile<D>::RS; }
+template <int D, int L, int NT = kThreads>
 __device__ __forceinline__ void put_rows(char* tile, const u32x4 (&c)[(Tile<D, NT>::NCH)]) {
 #pragma unroll
     for (int i = 0; i < Tile<D, NT>::NCH; ++i) {
         const int idx = (int)threadIdx.x + NT * i;
-        *reinterpret_cast<u32x4*>(tile + (idx / Tile<D>::CPR) * Tile<D>::RS + (idx % Tile<D>::CPR) * 16) = c[i];
+        const int row = idx / Tile<D>::CPR, ch = idx % Tile<D>::CPR;
+        *reinterpret_cast<u32x4*>(tile + row * row_bytes<D, L>() + (ch ^ swz<D, L>(row)) * 16) = c[i];
     }
 }
 
-// A operand with rows in sigma order: lane l supplies row sigma(l % 32), k-chunk 2ks + h.
-template <int D>
+// A operand with rows in sigma order from a ROWS tile: lane l supplies row sigma(l % 32),
+// k-chunk 2ks + h (stored at chunk (2ks + h) ^ kswz(sigma(l % 32)) = (2ks + h) ^ (l % 32 % KC)).
+template <int D, int L = ROWS>
 __device__ __forceinline__ u32x4 rd_rows(const char* tile, int ks, int lane) {
-    return *reinterpret_cast<const u32x4*>(tile + sigma(lane & 31) * Tile<D>::RS + (2 * ks + (lane >> 5)) * 16);
+    const int l32 = lane & 31;
+    const int x = L == PAD ? 0 : (l32 & (Tile<D>::CPR - 1));
+    return *reinterpret_cast<const u32x4*>(tile + sigma(l32) * row_bytes<D, L>() + (((2 * ks + (lane >> 5)) ^ x) * 16));
 }
-// A operand of a transposed tile: A[m = column 32db + l % 32][k = row 16kk + 8h .. + 7],
-// two transposing 8-byte reads (each 16-lane group reads 4 rows x 16 columns).
-template <int D>
+// A operand of a transposed COLS tile: A[m = column 32db + l % 32][k = row 16kk + 8h .. + 7],
+// two transposing 8-byte reads (each 16-lane group reads 4 rows x 16 columns); vswz depends
+// on the row modulo 4 only, the same for both reads.
+template <int D, int L = COLS>
 __device__ __forceinline__ u32x4 rd_cols(const char* tile, int db, int kk, int lane) {
     const int tg = lane >> 4, tc = lane & 15;
     const int row0 = 16 * kk + 8 * (tg >> 1) + (tc >> 2);
-    const int coff = (4 * db + 2 * (tg & 1) + ((tc & 3) >> 1)) * 16 + (tc & 1) * 8;
+    const int x = L == PAD ? 0 : vswz<D / 8>(row0);
+    const int coff = ((4 * db + 2 * (tg & 1) + ((tc & 3) >> 1)) ^ x) * 16 + (tc & 1) * 8;
     u32x4 out;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const char* addr = tile + (row0 + 4 * t) * Tile<D>::RS + coff;
+        const char* addr = tile + (row0 + 4 * t) * row_bytes<D, L>() + coff;
         const i16x4_t part = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<char*>(addr)));
         const u32x2 w = __builtin_bit_cast(u32x2, part);
         out[2 * t] = w[0];
@@ -128,8 +151,12 @@ __global__ __launch_bounds__(WV * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     constexpr int NT = WV * 64;
     using TL = Tile<D, NT>;
+    // Q (ROWS) for S; dO (COLS) for dV^T in the dV pass, (ROWS) for dP in the dK pass; Q
+    // again (COLS) for dK^T in the dK pass
+    constexpr int DO_L = PASS == 0 ? COLS : ROWS;
     __shared__ __attribute__((aligned(16))) char sQ[2][TL::BYTES];
     __shared__ __attribute__((aligned(16))) char sdO[2][TL::BYTES];
+    __shared__ __attribute__((aligned(16))) char sQc[PASS == 1 ? 2 : 1][PASS == 1 ? TL::BYTES : 16];
     __shared__ __attribute__((aligned(16))) float sL[2][32];
     __shared__ __attribute__((aligned(16))) float sD[2][32];
 
@@ -183,8 +210,9 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
         st.lse = (threadIdx.x < 32 && r < Nq) ? p.lse[bh * Nq + r] : 0.f;
     };
     auto commit = [&](int buf, const Stage& st) {
-        put_rows<D, NT>(sQ[buf], st.q);
-        put_rows<D, NT>(sdO[buf], st.dO);
+        put_rows<D, ROWS, NT>(sQ[buf], st.q);
+        put_rows<D, DO_L, NT>(sdO[buf], st.dO);
+        if constexpr (PASS == 1) put_rows<D, COLS, NT>(sQc[buf], st.q);
         // D_i = do_i . o_i: a chunk pair per thread, summed over the CPR chunks of a row
         // (consecutive lanes)
         if constexpr (PASS == 1)
@@ -241,7 +269,7 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
 #pragma unroll
             for (int db = 0; db < TL::DB; ++db) {
                 if constexpr (PASS == 0) acc[db] = Mfma<T>::mma(rd_cols<D>(sdO[buf], db, kk, lane), pf[kk], acc[db]);
-                else acc[db] = Mfma<T>::mma(rd_cols<D>(sQ[buf], db, kk, lane), dsf[kk], acc[db]);
+                else acc[db] = Mfma<T>::mma(rd_cols<D>(sQc[buf], db, kk, lane), dsf[kk], acc[db]);
             }
         if (it + 1 < nit) commit(buf ^ 1, other);
         __syncthreads();
@@ -268,8 +296,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dq_mfma_kernel(BwdProblem p) {
     using TL = Tile<D>;
-    __shared__ __attribute__((aligned(16))) char sK[2][TL::BYTES];
-    __shared__ __attribute__((aligned(16))) char sV[2][TL::BYTES];
+    // K and V tiles in the PAD layout (K read both ways from one copy)
+    __shared__ __attribute__((aligned(16))) char sK[2][TL::BYTESP];
+    __shared__ __attribute__((aligned(16))) char sV[2][TL::BYTESP];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -326,8 +355,8 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
         fetch_rows<T, D>(st.v, Vb, 32 * t, Nk, d);
     };
     auto commit = [&](int buf, const Stage& st) {
-        put_rows<D>(sK[buf], st.k);
-        put_rows<D>(sV[buf], st.v);
+        put_rows<D, PAD>(sK[buf], st.k);
+        put_rows<D, PAD>(sV[buf], st.v);
     };
     const int qw0 = i0 + 32 * wave;   // this wave's first query row
     auto body = [&](int t, Stage& mine, const Stage& other) {
@@ -337,8 +366,8 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < TL::KS; ++ks) {
-            s = Mfma<T>::mma(rd_rows<D>(sK[buf], ks, lane), qf[ks], s);
-            dp = Mfma<T>::mma(rd_rows<D>(sV[buf], ks, lane), dof[ks], dp);
+            s = Mfma<T>::mma(rd_rows<D, PAD>(sK[buf], ks, lane), qf[ks], s);
+            dp = Mfma<T>::mma(rd_rows<D, PAD>(sV[buf], ks, lane), dof[ks], dp);
         }
         // key tiles before the diagonal and away from the ends need no mask (uniform)
         const bool inner = qw0 + 32 <= Nq && 32 * t + 32 <= Nk && (!p.causal || 32 * t + 31 <= qw0);
@@ -361,7 +390,7 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int db = 0; db < TL::DB; ++db)
-                dq[db] = Mfma<T>::mma(rd_cols<D>(sK[buf], db, kk, lane), dsf[kk], dq[db]);
+                dq[db] = Mfma<T>::mma(rd_cols<D, PAD>(sK[buf], db, kk, lane), dsf[kk], dq[db]);
         if (t + 1 < nkt) commit(buf ^ 1, other);
         __syncthreads();
     };
