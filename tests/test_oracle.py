@@ -426,6 +426,24 @@ def test_workload_recipes():
     assert abs(c4.flops() - 249.34e9) / 249.34e9 < 1e-4
 
 
+def test_short_workload_recipe():
+    """The short cross-attention workload: 64 queries against 77 keys, 12 heads of 64
+    channels, batch 256, non-causal; FLOPs and compulsory bytes as the bench reports them."""
+    from workloads import SHORT_CONFIGS
+    s1 = SHORT_CONFIGS["s1_bf16_short_cross"]
+    assert (s1.batch, s1.heads_q, s1.heads_kv, s1.seqlen_q, s1.seqlen_k, s1.head_dim) == (256, 12, 12, 64, 77, 64)
+    assert not s1.causal and s1.softmax_scale == 0.125
+    assert s1.flops() == 4 * 64 * 12 * 256 * 64 * 77 == 3875536896
+    assert s1.bytes_compulsory() == 2 * 64 * 256 * (2 * 12 * 64 + 2 * 12 * 77) == 110886912
+    small = type(s1)("t", "bf16", 2, 4, 2, 5, 7, 8, False, seed=7)
+    q, k, v = small.inputs()
+    assert q.shape == (2, 4, 5, 8) and k.shape == (2, 2, 7, 8) and v.shape == (2, 2, 7, 8)
+    q2, k2, v2 = dense_inputs(2, 4, 2, 5, 7, 8, seed=7, dtype="bf16")
+    assert np.array_equal(q, q2) and np.array_equal(k, k2) and np.array_equal(v, v2)
+    causal = type(s1)("t", "bf16", 1, 1, 1, 6, 6, 8, True, seed=7)
+    assert causal.pairs() == 21
+
+
 def test_config1_full_oracle_runs():
     c1 = CONFIGS["c1_f32_dense"]
     q, k, v = c1.inputs()
