@@ -131,6 +131,15 @@ def test_short_lse():
         assert float(np.max(np.abs(host(out) - ro))) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Nq,Nk,d", [(512, 4, 4, 32, 40, 64), (1024, 4, 2, 32, 33, 64),
+                                            (600, 2, 2, 64, 96, 64), (300, 3, 3, 64, 77, 128)])
+def test_short_many_units(B, Hq, Hkv, Nq, Nk, d):
+    """Many (batch, kv head) units, several rounds of workgroups on the chip, GQA and plain,
+    head_dim 64 and 128, bf16 and fp16 with a negative scale."""
+    check(B, Hq, Hkv, Nq, Nk, d, "bf16", False, seed=B + Nk)
+    check(B, Hq, Hkv, Nq, Nk, d, "f16", False, scale=-0.2, seed=B + Nk + 1)
+
+
 def test_short_non_default_stream():
     check(4, 4, 4, 64, 77, 64, "bf16", False, seed=5, stream=torch.cuda.Stream())
 
