@@ -30,6 +30,12 @@ namespace aule {
 namespace {
 
 constexpr int kWaves = 4;
+// 32-row query tiles per iteration of the dV pass (one barrier per 128 rows; measured
+// 3.44 -> 3.31 -> 3.25 ms per step of the bf16 causal GQA backward for 1, 2, 4). The dK pass
+// keeps one: at 254 registers it has no room for a second score tile.
+#ifndef AULE_BWD_QH0
+#define AULE_BWD_QH0 4
+#endif
 constexpr int kThreads = kWaves * 64;
 constexpr float kLog2eF = 1.4426950408889634f;
 
@@ -146,19 +152,22 @@ __device__ __forceinline__ void store_rowT(T* row, const f32x16 (&acc)[Tile<D>::
 // fits two waves per SIMD, whose matrix products then overlap the other wave's
 // exponentials; the price is S computed twice. WV waves own 32 keys each: the Q / dO / O
 // rows of the group are read once per 32 * WV keys, so wider workgroups cut that traffic.
-template <typename T, int D, int PASS, int WV>
+// QH 32-row query tiles are staged per iteration (one barrier per 32 * QH rows); within an
+// iteration the halves' products and exponentials are independent until they accumulate.
+template <typename T, int D, int PASS, int WV, int QH>
 __global__ __launch_bounds__(WV * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     constexpr int NT = WV * 64;
+    constexpr int QR = 32 * QH;   // query rows per iteration
     using TL = Tile<D, NT>;
     // Q (ROWS) for S; dO (COLS) for dV^T in the dV pass, (ROWS) for dP in the dK pass; Q
     // again (COLS) for dK^T in the dK pass
     constexpr int DO_L = PASS == 0 ? COLS : ROWS;
-    __shared__ __attribute__((aligned(16))) char sQ[2][TL::BYTES];
-    __shared__ __attribute__((aligned(16))) char sdO[2][TL::BYTES];
-    __shared__ __attribute__((aligned(16))) char sQc[PASS == 1 ? 2 : 1][PASS == 1 ? TL::BYTES : 16];
-    __shared__ __attribute__((aligned(16))) float sL[2][32];
-    __shared__ __attribute__((aligned(16))) float sD[2][32];
+    __shared__ __attribute__((aligned(16))) char sQ[2][QH][TL::BYTES];
+    __shared__ __attribute__((aligned(16))) char sdO[2][QH][TL::BYTES];
+    __shared__ __attribute__((aligned(16))) char sQc[PASS == 1 ? 2 : 1][QH][PASS == 1 ? TL::BYTES : 16];
+    __shared__ __attribute__((aligned(16))) float sL[2][QR];
+    __shared__ __attribute__((aligned(16))) float sD[2][QR];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -174,11 +183,11 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     const int j0 = kb * 32 * WV;
     const int key = j0 + 32 * wave + ln;                 // this lane's key (B-operand column)
     const int64_t kv_off = ((int64_t)b * p.heads_kv + hk) * Nk * d;
-    // work: (query head g of the group, 32-row query tile), causal from the first key on.
+    // work: (query head g of the group, QR-row query tile), causal from the first key on.
     // With no query rows (nit == 0) only the zero gradients are written: q, k, v, o, do and
     // lse may then be null and are not read.
     const int i_start = p.causal ? j0 : 0;
-    const int ntile = Nq > i_start ? (Nq - i_start + 31) / 32 : 0;
+    const int ntile = Nq > i_start ? (Nq - i_start + QR - 1) / QR : 0;
     const int nit = G * ntile;
 
     u32x4 kf[TL::KS], vf[PASS == 1 ? TL::KS : 1];
@@ -196,50 +205,59 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     // into the set that held tile it while tile it + 1 (fetched an iteration earlier) is
     // committed to LDS, so each load has two iterations to arrive.
     struct Stage {
-        u32x4 q[TL::NCH], dO[TL::NCH], o[PASS == 1 ? TL::NCH : 1];
+        u32x4 q[QH][TL::NCH], dO[QH][TL::NCH], o[QH][PASS == 1 ? TL::NCH : 1];
         float lse;
     };
     auto fetch = [&](int it, Stage& st) {
-        const int g = it / ntile, i0 = i_start + 32 * (it - g * ntile);
+        const int g = it / ntile, i0 = i_start + QR * (it - g * ntile);
         const int64_t bh = (int64_t)b * p.heads_q + hk * G + g;
         const int64_t q_off = bh * Nq * d;
-        fetch_rows<T, D, NT>(st.q, static_cast<const T*>(p.q) + q_off, i0, Nq, d);
-        fetch_rows<T, D, NT>(st.dO, static_cast<const T*>(p.do_) + q_off, i0, Nq, d);
-        if constexpr (PASS == 1) fetch_rows<T, D, NT>(st.o, static_cast<const T*>(p.o) + q_off, i0, Nq, d);
+#pragma unroll
+        for (int hf = 0; hf < QH; ++hf) {
+            fetch_rows<T, D, NT>(st.q[hf], static_cast<const T*>(p.q) + q_off, i0 + 32 * hf, Nq, d);
+            fetch_rows<T, D, NT>(st.dO[hf], static_cast<const T*>(p.do_) + q_off, i0 + 32 * hf, Nq, d);
+            if constexpr (PASS == 1) fetch_rows<T, D, NT>(st.o[hf], static_cast<const T*>(p.o) + q_off, i0 + 32 * hf, Nq, d);
+        }
         const int r = i0 + (int)threadIdx.x;
-        st.lse = (threadIdx.x < 32 && r < Nq) ? p.lse[bh * Nq + r] : 0.f;
+        st.lse = ((int)threadIdx.x < QR && r < Nq) ? p.lse[bh * Nq + r] : 0.f;
     };
     auto commit = [&](int buf, const Stage& st) {
-        put_rows<D, ROWS, NT>(sQ[buf], st.q);
-        put_rows<D, DO_L, NT>(sdO[buf], st.dO);
-        if constexpr (PASS == 1) put_rows<D, COLS, NT>(sQc[buf], st.q);
-        // D_i = do_i . o_i: a chunk pair per thread, summed over the CPR chunks of a row
-        // (consecutive lanes)
-        if constexpr (PASS == 1)
 #pragma unroll
-        for (int i = 0; i < TL::NCH; ++i) {
-            float x = 0.f;
+        for (int hf = 0; hf < QH; ++hf) {
+            put_rows<D, ROWS, NT>(sQ[buf][hf], st.q[hf]);
+            put_rows<D, DO_L, NT>(sdO[buf][hf], st.dO[hf]);
+            if constexpr (PASS == 1) put_rows<D, COLS, NT>(sQc[buf][hf], st.q[hf]);
+            // D_i = do_i . o_i: a chunk pair per thread, summed over the CPR chunks of a row
+            // (consecutive lanes)
+            if constexpr (PASS == 1)
 #pragma unroll
-            for (int w = 0; w < 4; ++w) x = Mfma<T>::dot2(st.dO[i][w], st.o[i][w], x);
+            for (int i = 0; i < TL::NCH; ++i) {
+                float x = 0.f;
 #pragma unroll
-            for (int off = 1; off < TL::CPR; off <<= 1) x += __shfl_xor(x, off);
-            const int idx = (int)threadIdx.x + NT * i;
-            if (idx % TL::CPR == 0) sD[buf][idx / TL::CPR] = x;
+                for (int w = 0; w < 4; ++w) x = Mfma<T>::dot2(st.dO[hf][i][w], st.o[hf][i][w], x);
+#pragma unroll
+                for (int off = 1; off < TL::CPR; off <<= 1) x += __shfl_xor(x, off);
+                const int idx = (int)threadIdx.x + NT * i;
+                if (idx % TL::CPR == 0) sD[buf][32 * hf + idx / TL::CPR] = x;
+            }
         }
-        if (threadIdx.x < 32) sL[buf][threadIdx.x] = st.lse * kLog2eF;
+        if ((int)threadIdx.x < QR) sL[buf][threadIdx.x] = st.lse * kLog2eF;
     };
 
     const int kw0 = j0 + 32 * wave;   // this wave's first key
     auto body = [&](int it, Stage& mine, const Stage& other) {
         const int buf = it & 1;
-        const int g = it / ntile, i0 = i_start + 32 * (it - g * ntile);
+        const int g = it / ntile, i0q = i_start + QR * (it - g * ntile);
         if (it + 2 < nit) fetch(it + 2, mine);
+#pragma unroll
+        for (int hf = 0; hf < QH; ++hf) {
+        const int i0 = i0q + 32 * hf;
         // S = Q K^T, dP = dO V^T: register r holds query i0 + 16(r/8) + 8h + r%8, key `key`
         f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < TL::KS; ++ks) {
-            s = Mfma<T>::mma(rd_rows<D>(sQ[buf], ks, lane), kf[ks], s);
-            if constexpr (PASS == 1) dp = Mfma<T>::mma(rd_rows<D>(sdO[buf], ks, lane), vf[ks], dp);
+            s = Mfma<T>::mma(rd_rows<D>(sQ[buf][hf], ks, lane), kf[ks], s);
+            if constexpr (PASS == 1) dp = Mfma<T>::mma(rd_rows<D>(sdO[buf][hf], ks, lane), vf[ks], dp);
         }
         // tiles away from the diagonal and the ends need no mask (a uniform branch)
         const bool inner = i0 + 32 <= Nq && kw0 + 32 <= Nk && (!p.causal || kw0 + 31 <= i0);
@@ -252,9 +270,9 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
             for (int e = 0; e < 8; ++e) {
                 const int qi = i0 + q0 + e;
                 const bool vis = inner || (qi < Nq && key < Nk && (!p.causal || key <= qi));
-                const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -sL[buf][q0 + e])) : 0.f;
+                const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -sL[buf][32 * hf + q0 + e])) : 0.f;
                 pv[e] = pe;
-                dsv[e] = PASS == 1 ? pe * (dp[8 * kk + e] - sD[buf][q0 + e]) : 0.f;
+                dsv[e] = PASS == 1 ? pe * (dp[8 * kk + e] - sD[buf][32 * hf + q0 + e]) : 0.f;
             }
             if constexpr (PASS == 0)
                 pf[kk] = u32x4{Mfma<T>::pack2(pv[0], pv[1]), Mfma<T>::pack2(pv[2], pv[3]),
@@ -268,9 +286,10 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int db = 0; db < TL::DB; ++db) {
-                if constexpr (PASS == 0) acc[db] = Mfma<T>::mma(rd_cols<D>(sdO[buf], db, kk, lane), pf[kk], acc[db]);
-                else acc[db] = Mfma<T>::mma(rd_cols<D>(sQc[buf], db, kk, lane), dsf[kk], acc[db]);
+                if constexpr (PASS == 0) acc[db] = Mfma<T>::mma(rd_cols<D>(sdO[buf][hf], db, kk, lane), pf[kk], acc[db]);
+                else acc[db] = Mfma<T>::mma(rd_cols<D>(sQc[buf][hf], db, kk, lane), dsf[kk], acc[db]);
             }
+        }
         if (it + 1 < nit) commit(buf ^ 1, other);
         __syncthreads();
     };
@@ -419,10 +438,10 @@ hipError_t launch_typed(const BwdProblem& p, hipStream_t stream) {
     const int64_t nq = (int64_t)((p.seqlen_q + R - 1) / R) * p.heads_q * p.batch;
     if (nk > INT32_MAX || nq > INT32_MAX) return hipErrorInvalidConfiguration;
     dim3 gk((unsigned)nk);
-    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 0, WV>), gk, dim3(WV * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 0, WV, AULE_BWD_QH0>), gk, dim3(WV * 64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 1, WV>), gk, dim3(WV * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 1, WV, 1>), gk, dim3(WV * 64), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess || p.seqlen_q == 0) return e;   // no query rows: dK = dV = 0, no dQ
     dim3 gq((unsigned)nq);
