@@ -222,14 +222,27 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
             if (x >= n_qtiles * NG) return false;
             int t, g;
             if (NG % 8 == 0) {
-                // group-major within an XCD: all q-tiles of one group (longest first), then
-                // the next group, so one group's K/V is live in the XCD's L2 at a time (the
-                // snake order of the persistent workgroups keeps each one's causal work
-                // equal over every two rounds of a group)
+                // persistent: group-major within an XCD, all q-tiles of one group (longest
+                // first), then the next group, so one group's K/V is live in the XCD's L2 at
+                // a time (the snake order of the persistent workgroups keeps each one's
+                // causal work equal over every two rounds of a group)
                 const int per = NG / 8, xcd = x & 7, l = x >> 3;
-                const int gl = l / n_qtiles;
-                t = l - gl * n_qtiles;
-                g = xcd * per + gl;
+                if constexpr (PERSIST) {
+                    const int gl = l / n_qtiles;
+                    t = l - gl * n_qtiles;
+                    g = xcd * per + gl;
+                } else {
+                    // one workgroup per item, all resident at once when they fit: tile-rank
+                    // major, the first half of the ranks longest first and the second half
+                    // shortest first, so that the workgroups sharing a CU pair long with
+                    // short tiles (group-major here put two longest tiles on one CU: -12%
+                    // on the fp16 head_dim-64 causal workload; this order +5% over plain
+                    // rank-major)
+                    t = l / per;
+                    g = xcd * per + (l - t * per);
+                    const int half = (n_qtiles + 1) / 2;
+                    if (t >= half) t = n_qtiles - 1 - (t - half);
+                }
             } else {
                 t = x / NG;
                 g = x - t * NG;
