@@ -43,7 +43,8 @@ typedef enum {
 typedef enum {
     AULE_OK = 0,
     AULE_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size, misaligned or overlapping buffer, non-finite scale */
-    AULE_ERR_UNSUPPORTED = 2,      /* head_dim > 128 or not a multiple of 8, causal with seqlen_q != seqlen_k, unknown dtype */
+    AULE_ERR_UNSUPPORTED = 2,      /* head_dim > 128 or not a multiple of 8, causal with seqlen_q != seqlen_k, unknown dtype,
+                                      a 16-bit (sequence, head) slice of 1 GiB or more */
     AULE_ERR_HIP = 3               /* the HIP runtime reported an error at launch */
 } aule_status_t;
 
@@ -68,7 +69,9 @@ typedef enum {
  * batch == 0 or seqlen_q == 0 is an empty problem: AULE_OK, nothing launched, pointers not
  * inspected. Otherwise heads_q, heads_kv, seqlen_k >= 1 and heads_q % heads_kv == 0
  * (AULE_ERR_INVALID_ARGUMENT); 8 <= head_dim <= 128 with head_dim % 8 == 0
- * (AULE_ERR_UNSUPPORTED below or above that).
+ * (AULE_ERR_UNSUPPORTED below or above that). fp16/bf16 problems run on the matrix cores,
+ * whose kernels address one (batch, head) slice with 32-bit offsets: a slice of 1 GiB or
+ * more (about seqlen * head_dim * 2 bytes) is AULE_ERR_UNSUPPORTED. fp32 has no such bound.
  */
 aule_status_t aule_attn_fwd(const void* q, const void* k, const void* v, void* o,
                             int32_t batch, int32_t heads_q, int32_t heads_kv,
@@ -92,10 +95,14 @@ aule_status_t aule_attn_fwd(const void* q, const void* k, const void* v, void* o
  *                undefined behaviour of the caller, but the kernels clamp every index to
  *                [0, total_tokens) so it cannot make them read or write out of bounds.
  *   o          : [total_tokens, heads, head_dim] contiguous, dtype (written)
- *   max_seqlen : the caller's bound on the longest sequence (a hint; must be >= 0)
+ *   max_seqlen : the longest sequence length (as the varlen docstring defines it, the
+ *                batch's maximum); >= 1 when total_tokens > 0. Tokens of a sequence past
+ *                max_seqlen are neither read as keys nor written (their rows of o keep
+ *                their contents), so a bound below the true maximum truncates sequences.
  *
  * total_tokens == 0 is an empty problem: AULE_OK, nothing launched. Otherwise num_seqs >= 1,
- * heads >= 1, and the head_dim / dtype / scale rules of aule_attn_fwd apply.
+ * heads >= 1, max_seqlen >= 1, and the head_dim / dtype / scale rules of aule_attn_fwd apply,
+ * including the fp16/bf16 slice bound (here: max_seqlen * 3 * heads * head_dim * 2 bytes).
  */
 aule_status_t aule_attn_fwd_varlen(const void* qkv, const int32_t* cu_seqlens, void* o,
                                    int32_t num_seqs, int32_t total_tokens,

@@ -107,7 +107,7 @@ def test_fwd_empty_problems_are_noops(lib):
 @pytest.mark.parametrize("kw,status", [
     (dict(qkv=None), INV), (dict(cu=None), INV), (dict(o=None), INV),
     (dict(num_seqs=0), INV), (dict(num_seqs=-2), INV), (dict(total_tokens=-1), INV),
-    (dict(max_seqlen=-1), INV), (dict(heads=0), INV),
+    (dict(max_seqlen=-1), INV), (dict(max_seqlen=0), INV), (dict(heads=0), INV),
     (dict(head_dim=200), UNS), (dict(head_dim=12), UNS), (dict(dtype=3), UNS),
     (dict(scale=math.nan), INV),
     (dict(qkv=P["qkv"] + 4), INV), (dict(cu=P["cu"] + 2), INV),
@@ -116,6 +116,24 @@ def test_fwd_empty_problems_are_noops(lib):
 def test_varlen_rejects_invalid_arguments(lib, kw, status):
     assert varlen(**kw) == status
     assert aule.aule_last_error() != ""
+
+
+# far-apart fake pointers for problems whose tensors span gigabytes (never dereferenced)
+BIG = {"q": 0x100000000000, "k": 0x200000000000, "v": 0x300000000000, "o": 0x400000000000,
+       "qkv": 0x500000000000, "cu": 0x600000000000}
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_oversized_16bit_slices_are_refused(lib, dtype):
+    """A 16-bit problem whose (sequence, head) slice spans 1 GiB or more (past the
+    matrix-core kernels' 32-bit offsets) is refused before any launch, not sent to another
+    kernel; fp32 takes the vector-ALU kernel, which has no such bound."""
+    st = varlen(qkv=BIG["qkv"], cu=BIG["cu"], o=BIG["o"], num_seqs=1, total_tokens=100000,
+                max_seqlen=100000, heads=64, head_dim=128, dtype=dtype)
+    assert st == UNS and "1 GiB" in aule.aule_last_error()
+    st = fwd(q=BIG["q"], k=BIG["k"], v=BIG["v"], o=BIG["o"], batch=1, heads_q=1, heads_kv=1,
+             seqlen_q=5_000_000, seqlen_k=5_000_000, head_dim=128, causal=0, dtype=dtype)
+    assert st == UNS
 
 
 def test_varlen_empty_problem_is_noop(lib):

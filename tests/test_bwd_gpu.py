@@ -153,3 +153,67 @@ def test_bwd_non_default_stream():
     rdq, rdk, rdv = oracle.attention_ref_bwd(q, k, v, do, causal=True, scale=1 / 8)
     for got, ref in ((dq, rdq), (dk, rdk), (dv, rdv)):
         assert rel_err(host(got), ref) <= GTOL["f16"]
+
+
+def test_bwd_b1_shape_groups():
+    """The benchmarked backward shape (B4 Hq32 Hkv8 N4096 d128, bf16 causal GQA): every
+    gradient element of eight (batch, kv head) groups, one per kv head and spread over the
+    batch, against the oracle (a kv head's gradient sums over its own query group only)."""
+    c = BWD_CONFIGS["b1_bf16_causal_gqa_bwd"]
+    q, k, v = c.inputs()
+    do = c.grad()
+    sc = c.softmax_scale
+    tq, tk, tv, tdo = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(do, "bf16")
+    o, lse = aule.flash_attention(tq, tk, tv, causal=True, scale=sc, return_lse=True)
+    dq, dk, dv = aule.flash_attention_backward(tq, tk, tv, o, tdo, lse, causal=True, scale=sc)
+    torch.cuda.synchronize()
+    dq, dk, dv = host(dq), host(dk), host(dv)
+    G = c.heads_q // c.heads_kv
+    for hk in range(c.heads_kv):
+        b = hk % c.batch
+        sl = slice(hk * G, hk * G + G)
+        rdq, rdk, rdv = oracle.attention_ref_bwd(q[b:b + 1, sl], k[b:b + 1, hk:hk + 1],
+                                                 v[b:b + 1, hk:hk + 1], do[b:b + 1, sl],
+                                                 causal=True, scale=sc)
+        errs = {"dq": rel_err(dq[b:b + 1, sl], rdq), "dk": rel_err(dk[b:b + 1, hk:hk + 1], rdk),
+                "dv": rel_err(dv[b:b + 1, hk:hk + 1], rdv)}
+        print(f"  b={b} hk={hk} errors {errs}", flush=True)
+        for name, e in errs.items():
+            assert e <= GTOL["bf16"], f"{name} relative err {e} (b={b}, hk={hk})"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_autograd_sum_backward(dtype):
+    """flash_attention recorded for autograd: out.sum().backward() (dO = 1) fills q.grad,
+    k.grad and v.grad with the oracle's gradients (GQA: a kv head sums its query group)."""
+    B, Hq, Hkv, N, d = 2, 8, 2, 256, 64
+    q, k, v = dense_inputs(B, Hq, Hkv, N, N, d, seed=91, dtype=dtype)
+    tq, tk, tv = (dev(x, dtype).requires_grad_(True) for x in (q, k, v))
+    out = aule.flash_attention(tq, tk, tv, causal=True)
+    assert out.grad_fn is not None
+    out.sum().backward()
+    torch.cuda.synchronize()
+    sc = 1.0 / math.sqrt(d)
+    ref_o = oracle.attention_ref(q, k, v, causal=True, scale=sc)
+    assert rel_err(host(out.detach()), ref_o) <= GTOL[dtype]
+    rdq, rdk, rdv = oracle.attention_ref_bwd(q, k, v, np.ones(q.shape), causal=True, scale=sc)
+    for name, got, ref in (("dq", tq.grad, rdq), ("dk", tk.grad, rdk), ("dv", tv.grad, rdv)):
+        assert got is not None and got.dtype == TDT[dtype], name
+        e = rel_err(host(got), ref)
+        print(f"  autograd {dtype} {name} err {e:.3e}", flush=True)
+        assert e <= GTOL[dtype], f"{name} relative err {e}"
+
+
+def test_autograd_no_grad_and_lse():
+    """Without requires_grad (or under no_grad) the call records nothing; with return_lse the
+    log-sum-exp comes back non-differentiable next to a differentiable output."""
+    q, k, v = dense_inputs(1, 2, 2, 64, 64, 64, seed=92, dtype="bf16")
+    tq, tk, tv = dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16")
+    assert aule.flash_attention(tq, tk, tv).grad_fn is None
+    tq.requires_grad_(True)
+    with torch.no_grad():
+        assert aule.flash_attention(tq, tk, tv).grad_fn is None
+    o, lse = aule.flash_attention(tq, tk, tv, return_lse=True)
+    assert o.grad_fn is not None and not lse.requires_grad
+    with pytest.raises(ValueError):
+        aule.flash_attention(tq, tk, tv, out=torch.empty_like(tq))

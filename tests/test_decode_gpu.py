@@ -34,8 +34,7 @@ def host(t):
 
 
 def tolerance(dtype, scale, d):
-    if dtype == "f32":
-        return TOL[dtype] * max(1.0, abs(scale) * math.sqrt(d))
+    """The stated bar of the dtype (max abs error for O(1) outputs), at every scale."""
     return TOL[dtype]
 
 

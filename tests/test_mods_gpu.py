@@ -34,8 +34,7 @@ def dev(x, dtype):
 
 
 def tolerance(dtype, scale, d):
-    if dtype == "f32":
-        return TOL[dtype] * max(1.0, abs(scale) * math.sqrt(d))
+    """The stated bar of the dtype (max abs error for O(1) outputs), at every scale."""
     return TOL[dtype]
 
 
@@ -84,6 +83,14 @@ def test_window_causal(dtype, window):
                                     (300, 300)])
 def test_window_noncausal(dtype, window):
     check(LENGTHS, 2, 64, dtype, False, window=window, seed=window[1] + 11)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_window_int32_max(dtype, causal):
+    """Windows of 2^31 - 1 keys mask nothing (and must not overflow a row + window sum)."""
+    big = 2 ** 31 - 1
+    check(LENGTHS, 3, 128, dtype, causal, window=(big, 0 if causal else big), seed=8)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])

@@ -19,6 +19,10 @@ wrappers follow the pages' APIs:
 * ``flash_attention(..., return_lse=True)`` and ``flash_attention_backward(q, k, v, out, dout,
   lse)`` — the per-row log-sum-exp and the gradients (dq, dk, dv), the score matrix
   recomputed in the backward (FlashAttention-T commentary, FAQ 4, training bullet);
+  when q, k or v requires grad, ``flash_attention`` records itself for autograd, so
+  ``flash_attention(q, k, v, causal=True).sum().backward()`` fills q.grad, k.grad and v.grad
+  (the gradient example of the jdon.com Aule-Attention article): the forward runs
+  aule_attn_fwd_lse and keeps O and the LSE, the backward runs aule_attn_bwd;
 * ``flash_attention_decode(q, k, v, causal=True, scale=None, num_splits=0)`` — a few new
   queries against a key/value cache, split over the key range (FlashAttention-T
   commentary, FAQ 4: the KV cache processed in blocks at inference); causal masking is
@@ -34,8 +38,7 @@ import math
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# AULE_LIB points the binding at another build of the same library (variant comparisons)
-LIB_PATH = os.environ.get("AULE_LIB") or os.path.join(_PKG, "libaule_attn.so")
+LIB_PATH = os.path.join(_PKG, "libaule_attn.so")
 
 AULE_DTYPE_F32, AULE_DTYPE_F16, AULE_DTYPE_BF16 = 0, 1, 2
 AULE_OK, AULE_ERR_INVALID_ARGUMENT, AULE_ERR_UNSUPPORTED, AULE_ERR_HIP = 0, 1, 2, 3
@@ -195,11 +198,58 @@ def _need_gpu_tensor(name, t):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _autograd_fn():
+    """The torch.autograd.Function that records flash_attention for the backward (built on
+    first use so that importing this module does not import torch)."""
+    global _FlashAttentionFn
+    if _FlashAttentionFn is not None:
+        return _FlashAttentionFn
+    torch = _torch()
+
+    class FlashAttentionFn(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, causal, scale):
+            out, lse = _forward(q, k, v, causal, scale, None, True)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.causal, ctx.scale = causal, scale
+            ctx.mark_non_differentiable(lse)
+            return out, lse
+
+        @staticmethod
+        def backward(ctx, dout, _dlse):
+            q, k, v, out, lse = ctx.saved_tensors
+            if dout is None:
+                return None, None, None, None, None
+            # autograd may hand over an expanded (stride 0) gradient, e.g. from .sum()
+            dq, dk, dv = flash_attention_backward(q, k, v, out, dout.contiguous(), lse,
+                                                  causal=ctx.causal, scale=ctx.scale)
+            return dq, dk, dv, None, None
+
+    _FlashAttentionFn = FlashAttentionFn
+    return FlashAttentionFn
+
+
+_FlashAttentionFn = None
+
+
 def flash_attention(q, k, v, causal: bool = True, scale: float | None = None, out=None,
                     return_lse: bool = False):
     """O = softmax(scale * q k^T [+ causal mask]) v for q [B,Hq,N,d], k/v [B,Hkv,Nk,d].
     With ``return_lse`` also returns the fp32 per-row log-sum-exp [B,Hq,N] the backward
-    needs: (out, lse)."""
+    needs: (out, lse). When gradients are enabled and q, k or v requires grad the call is
+    recorded for autograd (``out`` must then be None)."""
+    torch = _torch()
+    if torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v)):
+        if out is not None:
+            raise ValueError("out= cannot be used when q, k or v requires grad")
+        if scale is None:
+            scale = 1.0 / math.sqrt(q.shape[-1])
+        o, lse = _autograd_fn().apply(q, k, v, bool(causal), float(scale))
+        return (o, lse) if return_lse else o
+    return _forward(q, k, v, causal, scale, out, return_lse)
+
+
+def _forward(q, k, v, causal, scale, out, return_lse):
     torch = _torch()
     for name, t in (("q", q), ("k", k), ("v", v)):
         _need_gpu_tensor(name, t)
@@ -319,8 +369,9 @@ def flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen, dropout_p=0.0,
     softcap * tanh(x / softcap), ``alibi_slopes`` (fp32 [heads] or [batch, heads] on the
     device) subtracts slope * |i - j|.
 
-    ``validate=True`` also checks cu_seqlens against total_tokens and max_seqlen, which
-    reads it back to the host (a synchronisation)."""
+    ``max_seqlen`` must be at least the longest sequence: tokens of a sequence past it are
+    neither read as keys nor written. ``validate=True`` also checks cu_seqlens against
+    total_tokens and max_seqlen, which reads it back to the host (a synchronisation)."""
     torch = _torch()
     if dropout_p != 0.0:
         raise NotImplementedError("dropout is not supported")

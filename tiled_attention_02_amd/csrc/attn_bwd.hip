@@ -222,11 +222,7 @@ hipError_t launch_dim(const BwdProblem& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_bwd(const BwdProblem& p, Dtype dt, hipStream_t stream) {
-    switch (dt) {
-        case Dtype::F32: return launch_dim<float>(p, stream);
-        case Dtype::F16: return launch_dim<f16_t>(p, stream);
-        case Dtype::BF16: return launch_dim<bf16_t>(p, stream);
-    }
+    if (dt == Dtype::F32) return launch_dim<float>(p, stream);   // fp32 only
     return hipErrorInvalidValue;
 }
 

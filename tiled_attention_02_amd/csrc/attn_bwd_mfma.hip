@@ -6,21 +6,23 @@
 // dP = do_i.v_j, dS = P (dP - D_i) with D_i = do_i.o_i; dV_j += P dO_i,
 // dK_j += scale dS q_i, dQ_i += scale dS k_j.
 //
-// Two kernels, no atomics (deterministic), 4 waves per workgroup, 32-row / 32-key steps:
-//   * dK/dV: wave w owns 32 keys (K and V rows held as B operands in registers) and the
-//     transposed accumulators dK^T, dV^T (d x 32 keys). The workgroup walks every query
-//     head of its GQA group and every 32-row query tile (causal: from its first key on);
-//     Q and dO tiles go through LDS (double-buffered, the next tile's global loads issued
-//     before the current tile's products), D_i is formed from the O and dO chunks as they
-//     arrive. Per tile: S = Q K^T and dP = dO V^T with Q / dO rows fed in sigma order, so
-//     P and dS leave the accumulators already in the B-operand layout of
-//     dV^T += dO^T P and dK^T += Q^T dS, whose A operands (dO^T, Q^T) are transposing LDS
-//     reads (ds_read_b64_tr_b16).
-//   * dQ: wave w owns 32 query rows (Q and dO rows in registers, LSE_i and D_i per lane);
-//     the workgroup walks the key tiles (causal: up to its last row). Per tile: S^T = K Q^T,
-//     dP^T = V dO^T with K / V rows in sigma order, then dQ^T += K^T dS^T with K^T read
-//     transposed from LDS.
-// LDS tiles are row-major [32][D] with one 16-byte pad per row.
+// Three launches, no atomics (deterministic), 32-row / 32-key steps:
+//   * dV pass and dK pass (one kernel, two instantiations; WV = 8 waves per workgroup at
+//     head_dim 128, 4 at 64): wave w owns 32 keys (its K rows and, for dK, its V rows held
+//     as B operands in registers) and one transposed accumulator (dV^T or dK^T, d x 32
+//     keys). The workgroup walks every query head of its GQA group and every 32-row query
+//     tile (causal: from its first key on); Q and dO tiles go through LDS, double-buffered,
+//     their global loads issued two iterations ahead. Per tile: S = Q K^T (and dP = dO V^T)
+//     with Q / dO rows fed in sigma order, so P and dS leave the accumulators already in the
+//     B-operand layout of dV^T += dO^T P and dK^T += Q^T dS, whose A operands (dO^T, Q^T)
+//     are transposing LDS reads (ds_read_b64_tr_b16). The dK pass forms D_i from the O and
+//     dO chunks as they are staged. The dV pass stages four 32-row query tiles per barrier.
+//   * dQ (4 waves): wave w owns 32 query rows (Q and dO rows in registers, LSE_i and D_i per
+//     lane); the workgroup walks the key tiles (causal: up to its last row). Per tile:
+//     S^T = K Q^T, dP^T = V dO^T with K / V rows in sigma order, then dQ^T += K^T dS^T with
+//     K^T read transposed from LDS.
+// The dQ kernel keeps K / V tiles row-major [32][D] with one 16-byte pad per row; the dK / dV
+// passes store each staged tile XOR-swizzled in the layout of the read that uses it.
 #include <hip/hip_runtime.h>
 
 #include "attn_bwd.h"
@@ -33,9 +35,7 @@ constexpr int kWaves = 4;
 // 32-row query tiles per iteration of the dV pass (one barrier per 128 rows; measured
 // 3.44 -> 3.31 -> 3.25 ms per step of the bf16 causal GQA backward for 1, 2, 4). The dK pass
 // keeps one: at 254 registers it has no room for a second score tile.
-#ifndef AULE_BWD_QH0
-#define AULE_BWD_QH0 4
-#endif
+constexpr int kDvTiles = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLog2eF = 1.4426950408889634f;
 
@@ -438,7 +438,7 @@ hipError_t launch_typed(const BwdProblem& p, hipStream_t stream) {
     const int64_t nq = (int64_t)((p.seqlen_q + R - 1) / R) * p.heads_q * p.batch;
     if (nk > INT32_MAX || nq > INT32_MAX) return hipErrorInvalidConfiguration;
     dim3 gk((unsigned)nk);
-    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 0, WV, AULE_BWD_QH0>), gk, dim3(WV * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 0, WV, kDvTiles>), gk, dim3(WV * 64), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 1, WV, 1>), gk, dim3(WV * 64), 0, stream, p);

@@ -228,8 +228,9 @@ __global__ __launch_bounds__(kThreads) void attn_decode_partial_kernel(DecodePro
         // ---- scores: lane = key of the tile, wave rows r = wave + 4q (in log2 units)
         const int key = k0 + lane;
         float s[RPW];
+        float s1[RPW], s2[RPW], s3[RPW];   // fp32: four partial sums, combined pairwise
 #pragma unroll
-        for (int q = 0; q < RPW; ++q) s[q] = 0.f;
+        for (int q = 0; q < RPW; ++q) s[q] = s1[q] = s2[q] = s3[q] = 0.f;
         if (lane < TK) {
 #pragma unroll 4
             for (int cc = 0; cc < CPR; ++cc) {
@@ -253,9 +254,9 @@ __global__ __launch_bounds__(kThreads) void attn_decode_partial_kernel(DecodePro
                         if (r < R) {
                             const f32x4 qq = *reinterpret_cast<const f32x4*>(&sQ[r][cc * EPC]);
                             s[q] = fmaf(kf[0], qq[0], s[q]);
-                            s[q] = fmaf(kf[1], qq[1], s[q]);
-                            s[q] = fmaf(kf[2], qq[2], s[q]);
-                            s[q] = fmaf(kf[3], qq[3], s[q]);
+                            s1[q] = fmaf(kf[1], qq[1], s1[q]);
+                            s2[q] = fmaf(kf[2], qq[2], s2[q]);
+                            s3[q] = fmaf(kf[3], qq[3], s3[q]);
                         }
                     }
                 }
@@ -263,6 +264,9 @@ __global__ __launch_bounds__(kThreads) void attn_decode_partial_kernel(DecodePro
             if constexpr (HALF) {
 #pragma unroll
                 for (int q = 0; q < RPW; ++q) s[q] *= c;
+            } else {
+#pragma unroll
+                for (int q = 0; q < RPW; ++q) s[q] = (s[q] + s1[q]) + (s2[q] + s3[q]);
             }
         }
         // ---- online softmax per row (wave-uniform branches). 16-bit path: P is packed in

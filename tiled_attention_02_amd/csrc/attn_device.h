@@ -41,11 +41,14 @@ __device__ __forceinline__ int clamp_tok(int x, int total) {
 // which never overlap and all lie below floor(T / BM) + num_seqs, the grid size. A
 // workgroup finds its sequence by binary search over first(.) and exits if its id falls in
 // the gap after the sequence's last tile. Every cu value is clamped to [0, T], so even a
-// malformed cu_seqlens cannot move a tile outside the packed tensor. When `reverse` is
-// set the tiles of a sequence are handed out last-tile-first (the longest causal tiles
-// start earliest).
+// malformed cu_seqlens cannot move a tile outside the packed tensor, and a sequence's length
+// is clamped to max_len (the caller's max_seqlen): tokens past it are neither read as keys
+// nor written, and the kernels' per-sequence 32-bit offsets stay within the bound the host
+// checked. When `reverse` is set the tiles of a sequence are handed out last-tile-first (the
+// longest causal tiles start earliest).
 __device__ __forceinline__ TileSlot locate_varlen_tile(const int32_t* __restrict__ cu, int nseq,
-                                                       int total, int BM, int x, bool reverse) {
+                                                       int total, int max_len, int BM, int x,
+                                                       bool reverse) {
     int lo = 0, hi = nseq - 1;
     while (lo < hi) {
         int mid = (lo + hi + 1) >> 1;
@@ -56,6 +59,7 @@ __device__ __forceinline__ TileSlot locate_varlen_tile(const int32_t* __restrict
     int start = clamp_tok(cu[lo], total);
     int end = clamp_tok(cu[lo + 1], total);
     int len = end > start ? end - start : 0;
+    len = len < max_len ? len : max_len;
     int local = x - (start / BM + lo);
     int ntiles = (len + BM - 1) / BM;
     t.valid = local < ntiles;

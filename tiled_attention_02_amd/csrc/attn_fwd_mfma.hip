@@ -7,15 +7,20 @@
 // laid out for 64-wide wavefronts and v_mfma_f32_32x32x16_{bf16,f16}.
 //
 // Work split
-//   workgroup = 4 waves; wave = 64 query rows (two 32-row blocks "nb") of one query head.
-//   GH query heads that share one K/V head run in the same workgroup (GQA), the other
-//   4/GH waves take further 64-row blocks, so one K/V tile in LDS serves 4 x 64 query rows.
-//   K/V tiles of BN = 64 keys, double-buffered in LDS. They are copied global -> LDS with
-//   buffer_load_dwordx4 ... lds (no register staging): each wave instruction fills 1 KiB of
-//   LDS contiguously, and every lane picks the global 16-byte chunk that belongs at its LDS
-//   slot, so the LDS image is XOR-swizzled against bank conflicts while the global reads stay
-//   whole rows. The buffer descriptor's size check turns rows past the sequence end and
-//   columns past head_dim into zeros.
+//   Two kernel forms, chosen by shape (launch_gh):
+//   * dense problems at head_dim 128: workgroup = 8 waves (two per SIMD, so one wave's
+//     softmax can run under the other's matrix products); wave = 32 query rows of one query
+//     head; GH query heads that share one K/V head run in the same workgroup (GQA) and the
+//     other 8/GH waves take further 32-row blocks, so one K/V tile in LDS serves 256 query
+//     rows. K/V tiles of 128 keys, double-buffered; persistent workgroups (one per CU), each
+//     walking several work items.
+//   * varlen problems and head_dim <= 64: workgroup = 4 waves over 128 query rows, K/V tiles
+//     of 64 keys, double-buffered, two workgroups per CU, one workgroup per work item.
+//   K/V tiles are copied global -> LDS with buffer_load_dwordx4 ... lds (no register
+//   staging): each wave instruction fills 1 KiB of LDS contiguously, and every lane picks
+//   the global 16-byte chunk that belongs at its LDS slot, so the LDS image is XOR-swizzled
+//   against bank conflicts while the global reads stay whole rows. The buffer descriptor's
+//   size check turns rows past the sequence end and columns past head_dim into zeros.
 //
 // Transposed products
 //   S^T = K Q^T : A = K tile rows (from LDS), B = Q^T (registers, loaded once). In the
@@ -41,7 +46,6 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
-#include <cstdlib>
 
 #include "attn_device.h"
 #include "attn_mfma.h"
@@ -51,12 +55,7 @@ namespace {
 
 [[maybe_unused]] constexpr float kRescaleSlack = 8.0f; // log2 units
 [[maybe_unused]] constexpr float kSlackExp = 256.0f;   // 2^kRescaleSlack
-#ifndef AULE_DMA_PARTS
-#define AULE_DMA_PARTS 4
-#endif
-#ifndef AULE_SOFTMAX_FAST
-#define AULE_SOFTMAX_FAST 1
-#endif
+constexpr int kCopyParts = 4;                           // pieces of one K/V tile copy
 
 #if defined(__HIP_DEVICE_COMPILE__)
 // Start the global -> LDS copy of one K/V tile: NI 16-byte loads per lane for each of K and
@@ -119,9 +118,8 @@ __device__ __forceinline__ void lds_barrier() {
 // type so that every buffer index stays a compile-time constant.
 template <int P> struct Parity { static constexpr int value = P; };
 
-// TB: keys per K/V tile. Eight-wave workgroups with 64-key tiles use three LDS buffers
-// (copies requested two tiles ahead); every other shape uses two (one tile ahead).
-// PERSIST (dense problems, two buffers): the grid holds one workgroup per CU and each walks
+// TB: keys per K/V tile, double-buffered in LDS (the copy of tile t+1 runs during tile t).
+// PERSIST (dense problems): the grid holds one workgroup per CU and each walks
 // several work items, issuing the next item's first K/V tile copy and its Q loads while it
 // finishes the current item, so that their latency and the workgroup launch gap are hidden.
 template <typename T, int D, int WAVES, int NB, int GH, int TB, bool PERSIST, bool CAUSAL, bool VARLEN,
@@ -138,12 +136,12 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     constexpr int DB = D / 32;                   // 32-row d-blocks of O^T
     constexpr int kBN = TB;                      // keys per K/V tile
     constexpr int SPT = TB / 32;                 // 32-key sub-steps per tile
-    constexpr int NBUF = (TB == 64 && WAVES == 8) ? 3 : 2;   // LDS tile buffers
-    constexpr int AHEAD = NBUF - 1;              // tiles requested ahead
-    constexpr int DMA_PARTS = AULE_DMA_PARTS < SPT ? AULE_DMA_PARTS : SPT;   // pieces of a tile copy
+    constexpr int NBUF = 2;                      // LDS tile buffers (double buffering)
+    constexpr int AHEAD = 1;                     // tiles requested ahead
+    constexpr int DMA_PARTS = kCopyParts < SPT ? kCopyParts : SPT;   // pieces of a tile copy
     constexpr int NSTORE = NB * DB * 4;          // O store instructions per wave and work item
     static_assert(TB == 64 || TB == 128, "tile of 64 or 128 keys");
-    static_assert(!PERSIST || (NBUF == 2 && !VARLEN), "persistent form: two buffers, dense problems");
+    static_assert(!PERSIST || !VARLEN, "persistent form: dense problems");
     constexpr int TILE_CHUNKS = kBN * KC;        // 16-byte chunks per K (or V) tile
     constexpr int NI = TILE_CHUNKS / kThreads;   // load instructions per wave per tile
     static_assert(NI >= 1 && TILE_CHUNKS % kThreads == 0, "tile must split evenly over the waves");
@@ -209,7 +207,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         int bidx, hq0, tile, Lq, Lk;
         int64_t tok0 = 0;
         if constexpr (VARLEN) {
-            TileSlot s = locate_varlen_tile(p.cu_seqlens, p.batch, p.total_tokens, BMW, x, CAUSAL);
+            TileSlot s = locate_varlen_tile(p.cu_seqlens, p.batch, p.total_tokens, p.max_seqlen, BMW, x, CAUSAL);
             if (!s.valid) return false;
             bidx = s.seq; tok0 = s.tok0; tile = s.tile; Lq = s.len_q; Lk = s.len_k;
             hq0 = vy * GH;
@@ -497,7 +495,6 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         return lsum;
     };
     auto softmax = [&](const f32x16 (&acc)[NB], u32x4 (&pf)[2][NB], Soft& st) {
-#if AULE_SOFTMAX_FAST
         // Fast path: exponentiate against the current reference max right away. If no
         // lane's partial row sum exceeds 2^slack, no single P does, so no score exceeds the
         // reference by more than the slack and the full path below would keep the reference
@@ -522,7 +519,6 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                 return;
             }
         }
-#endif
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             float mx = -INFINITY;
@@ -624,7 +620,6 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                 // at tile 0 of a later item the previous item's NSTORE stores are the newest
                 // memory operations and may stay in flight
                 if (PERSIST && t == 0 && !first) wait_vmcnt_barrier<NSTORE>();
-                else if (AHEAD == 2 && t + 1 < cur.n_kt) wait_vmcnt_barrier<2 * NI>();   // tile t+1 may stay in flight
                 else wait_vmcnt_barrier<0>();
                 // Fragment reads run one step ahead of their use: after the S^T products of
                 // sub-step i are issued, the V fragments of i and the K fragments of i+1 are
@@ -688,22 +683,6 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 
 int heads_per_group(int group) { return (group % 4 == 0) ? 4 : (group % 2 == 0) ? 2 : 1; }
 
-// Kernel form: 0 straight with 64-key tiles (three buffers), 1 straight with 128-key tiles
-// (two buffers), 4 straight with 64-key tiles in 4-wave workgroups (two workgroups per CU),
-// 5 persistent over 128-key tiles (dense only; varlen problems take form 1 instead).
-// Default: 5 for dense problems at head_dim 128, 4 for varlen problems and head_dim <= 64,
-// where the 128-row workgroups balance the causal work better (measured on the bf16
-// varlen and fp16 head_dim-64 causal workloads: +6% and +10%; -3% on the bf16 GQA
-// head_dim-128 one). AULE_MFMA_LOOP overrides it for comparisons; -1: no override.
-int mfma_loop() {
-    static const int v = [] {
-        const char* e = std::getenv("AULE_MFMA_LOOP");
-        const int v = e ? std::atoi(e) : -1;
-        return (v == 0 || v == 1 || v == 4 || v == 5) ? v : -1;
-    }();
-    return v;
-}
-
 // workgroups that fit on the device at once for the persistent form (one per CU)
 int resident_workgroups() {
     int dev = 0, n = 0;
@@ -746,21 +725,17 @@ hipError_t launch_gh(const AttnProblem& p, hipStream_t stream) {
         // window, soft cap 50 and ALiBi
         if (p.mods) return launch_cfg<T, D, 4, 1, 1, 64, false, CAUSAL, true, true>(p, stream);
     }
-    int form = mfma_loop();
-    if (form < 0) form = (VARLEN || D <= 64) ? 4 : 5;
-    if (VARLEN && form == 5) form = 1;
-    switch (form * 3 + g) {
-        case 0: return launch_cfg<T, D, 8, 1, 1, 64, false, CAUSAL, VARLEN>(p, stream);
-        case 1: return launch_cfg<T, D, 8, 1, 2, 64, false, CAUSAL, VARLEN>(p, stream);
-        case 2: return launch_cfg<T, D, 8, 1, 4, 64, false, CAUSAL, VARLEN>(p, stream);
-        case 3: return launch_cfg<T, D, 8, 1, 1, 128, false, CAUSAL, VARLEN>(p, stream);
-        case 4: return launch_cfg<T, D, 8, 1, 2, 128, false, CAUSAL, VARLEN>(p, stream);
-        case 5: return launch_cfg<T, D, 8, 1, 4, 128, false, CAUSAL, VARLEN>(p, stream);
-        case 12: return launch_cfg<T, D, 4, 1, 1, 64, false, CAUSAL, VARLEN>(p, stream);
-        case 13: return launch_cfg<T, D, 4, 1, 2, 64, false, CAUSAL, VARLEN>(p, stream);
-        case 14: return launch_cfg<T, D, 4, 1, 4, 64, false, CAUSAL, VARLEN>(p, stream);
-    }
-    if constexpr (!VARLEN) {
+    // dense problems at head_dim 128: persistent 8-wave workgroups over 128-key tiles;
+    // varlen problems and head_dim <= 64: 4-wave workgroups over 64-key tiles, where the
+    // 128-row workgroups balance the causal work better (measured on the bf16 varlen and fp16
+    // head_dim-64 causal workloads: +6% and +10% over the 8-wave form)
+    if constexpr (VARLEN || D <= 64) {
+        switch (g) {
+            case 0: return launch_cfg<T, D, 4, 1, 1, 64, false, CAUSAL, VARLEN>(p, stream);
+            case 1: return launch_cfg<T, D, 4, 1, 2, 64, false, CAUSAL, VARLEN>(p, stream);
+            case 2: return launch_cfg<T, D, 4, 1, 4, 64, false, CAUSAL, VARLEN>(p, stream);
+        }
+    } else {
         switch (g) {
             case 0: return launch_cfg<T, D, 8, 1, 1, 128, true, CAUSAL, false>(p, stream);
             case 1: return launch_cfg<T, D, 8, 1, 2, 128, true, CAUSAL, false>(p, stream);
@@ -787,11 +762,12 @@ hipError_t launch_t(const AttnProblem& p, hipStream_t stream) {
 
 bool mfma_supports(const AttnProblem& p, Dtype dt) {
     if (!(dt == Dtype::F16 || dt == Dtype::BF16) || p.head_dim > 128 || p.head_dim % 8 != 0) return false;
-    // K/V copies address one (sequence, kv head) slice with 32-bit buffer offsets; keep the
-    // slice plus one tile of offset headroom below 2^30 bytes.
-    // The same holds for the Q loads and O stores, which address one slice of Q / O.
-    const int64_t rows_k = p.cu_seqlens ? p.total_tokens : p.seqlen_k;
-    const int64_t rows_q = p.cu_seqlens ? p.total_tokens : p.seqlen_q;
+    // K/V copies, Q loads and O stores address one (sequence, head) slice with 32-bit buffer
+    // offsets from the slice's first row (64-bit pointers get there); keep the slice plus
+    // one tile of offset headroom below 2^30 bytes. A varlen slice is at most max_seqlen rows
+    // (the kernels clamp every sequence to it).
+    const int64_t rows_k = p.cu_seqlens ? p.max_seqlen : p.seqlen_k;
+    const int64_t rows_q = p.cu_seqlens ? p.max_seqlen : p.seqlen_q;
     const int64_t stride_k = p.k_rstride > p.v_rstride ? p.k_rstride : p.v_rstride;
     const int64_t stride_q = p.q_rstride > p.o_rstride ? p.q_rstride : p.o_rstride;
     const int64_t limit = int64_t(1) << 30;

@@ -22,7 +22,6 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
-#include <cstdlib>
 
 #include "attn_device.h"
 #include "attn_mfma.h"
@@ -220,15 +219,6 @@ void attn_fwd_short_kernel(AttnProblem p, int n_rb) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-// AULE_SHORT=0 sends every problem to the tiled kernel (for comparisons; read once).
-bool short_enabled() {
-    static const bool v = [] {
-        const char* e = std::getenv("AULE_SHORT");
-        return !(e && e[0] == '0');
-    }();
-    return v;
-}
-
 template <typename T, int D, int WAVES, bool CAUSAL>
 hipError_t launch_short_cfg(const AttnProblem& p, hipStream_t stream) {
     const int n_rb = (p.seqlen_q + 31) / 32;
@@ -257,7 +247,6 @@ hipError_t launch_short_t(const AttnProblem& p, hipStream_t stream) {
 }  // namespace
 
 bool short_supports(const AttnProblem& p, Dtype dt) {
-    if (!short_enabled()) return false;
     if (!(dt == Dtype::F16 || dt == Dtype::BF16) || p.cu_seqlens || p.mods) return false;
     if (p.head_dim > 128 || p.head_dim % 8 != 0) return false;
     if (p.seqlen_k < 1 || p.seqlen_k > kShortMaxKeys || p.seqlen_q < 1) return false;

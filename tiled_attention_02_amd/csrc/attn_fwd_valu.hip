@@ -1,7 +1,7 @@
 // Tiled attention forward on the vector ALUs, fp32 arithmetic throughout.
 //
-// This is the fp32 path (no reduced-precision matrix instruction touches fp32 inputs) and
-// the fallback for head dims the MFMA kernel does not instantiate. It follows the
+// This is the fp32 path (no reduced-precision matrix instruction touches fp32 inputs). It
+// follows the
 // FlashAttention block loop of the xxqk.cn article "Attention算子实战：从CUDA优化到昇腾/CANN部署"
 // (section 2.2): a Q tile stays on chip, K/V tiles stream through LDS, each tile updates a
 // running row max m and row sum l (online softmax, FlashAttention-T commentary on
@@ -42,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_valu_kernel(AttnProblem p) 
 
     TileSlot slot;
     if constexpr (VARLEN) {
-        slot = locate_varlen_tile(p.cu_seqlens, p.batch, p.total_tokens, kBM, blockIdx.x, false);
+        slot = locate_varlen_tile(p.cu_seqlens, p.batch, p.total_tokens, p.max_seqlen, kBM, blockIdx.x, false);
         if (!slot.valid) return;
     } else {
         slot.valid = 1;
@@ -105,9 +105,16 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_valu_kernel(AttnProblem p) 
 #pragma unroll
         for (int u = 0; u < kBN / kTPR; ++u) {
             int jj = c + kTPR * u;
-            float dot = 0.f;
-#pragma unroll 8
-            for (int dd = 0; dd < DMAX; ++dd) dot = fmaf(sQ[r][dd], sK[jj][dd], dot);
+            // eight partial sums over interleaved columns, combined pairwise: about an eighth
+            // of the rounding error of one serial chain over head_dim terms
+            float part[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part[e] = 0.f;
+#pragma unroll
+            for (int dd = 0; dd < DMAX; dd += 8)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) part[e] = fmaf(sQ[r][dd + e], sK[jj][dd + e], part[e]);
+            const float dot = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
             int j = j0 + jj;
             bool masked = (j >= Lk) || (p.causal && j > i);
             if constexpr (MODS) {
@@ -144,9 +151,13 @@ __global__ __launch_bounds__(kThreads) void attn_fwd_valu_kernel(AttnProblem p) 
 #pragma unroll
         for (int u = 0; u < DMAX / kTPR; ++u) {
             int dd = c + kTPR * u;
-            float a = acc[u] * alpha;
-            for (int jj = 0; jj < kBN; ++jj) a = fmaf(sP[r][jj], sV[jj][dd], a);
-            acc[u] = a;
+            float a0 = 0.f, a1 = 0.f;   // the tile's contribution in two chains
+#pragma unroll 8
+            for (int jj = 0; jj < kBN; jj += 2) {
+                a0 = fmaf(sP[r][jj], sV[jj][dd], a0);
+                a1 = fmaf(sP[r][jj + 1], sV[jj + 1][dd], a1);
+            }
+            acc[u] = fmaf(acc[u], alpha, a0 + a1);
         }
     }
 
@@ -187,11 +198,7 @@ hipError_t launch_dim(const AttnProblem& p, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_attn_fwd_valu(const AttnProblem& p, Dtype dt, hipStream_t stream) {
-    switch (dt) {
-        case Dtype::F32: return launch_dim<float>(p, stream);
-        case Dtype::F16: return launch_dim<f16_t>(p, stream);
-        case Dtype::BF16: return launch_dim<bf16_t>(p, stream);
-    }
+    if (dt == Dtype::F32) return launch_dim<float>(p, stream);   // fp32 only
     return hipErrorInvalidValue;
 }
 

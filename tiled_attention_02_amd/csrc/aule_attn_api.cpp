@@ -8,7 +8,6 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
-#include <cstdlib>
 
 #include "aule_attn.h"
 #include "attn_bwd.h"
@@ -36,16 +35,6 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
     return a0 < b0 + nb && b0 < a0 + na;
 }
 
-// AULE_FORCE_VALU=1 routes fp16/bf16 through the vector-ALU kernel (a debugging aid for
-// comparing the two kernels; read once per process).
-bool force_valu() {
-    static const bool v = [] {
-        const char* e = std::getenv("AULE_FORCE_VALU");
-        return e && e[0] == '1';
-    }();
-    return v;
-}
-
 aule_status_t check_common(int32_t head_dim, float scale, aule_dtype_t dtype) {
     if (dtype != AULE_DTYPE_F32 && dtype != AULE_DTYPE_F16 && dtype != AULE_DTYPE_BF16)
         return fail(AULE_ERR_UNSUPPORTED, "unknown dtype %d", (int)dtype);
@@ -58,23 +47,28 @@ aule_status_t check_common(int32_t head_dim, float scale, aule_dtype_t dtype) {
     return AULE_OK;
 }
 
-// fp16/bf16 backward on the matrix cores, fp32 (or AULE_FORCE_VALU=1) on the vector ALUs
+// fp16/bf16 backward on the matrix cores, fp32 on the vector ALUs
 hipError_t launch_bwd(const aule::BwdProblem& p, aule_dtype_t dtype, hipStream_t stream) {
     const aule::Dtype dt = static_cast<aule::Dtype>(dtype);
-    if (!force_valu() && (dt == aule::Dtype::F16 || dt == aule::Dtype::BF16))
-        return aule::launch_attn_bwd_mfma(p, dt, stream);
+    if (dt == aule::Dtype::F16 || dt == aule::Dtype::BF16) return aule::launch_attn_bwd_mfma(p, dt, stream);
     return aule::launch_attn_bwd(p, dt, stream);
 }
 
+// fp32 runs on the vector-ALU kernel; fp16/bf16 on the matrix cores: the short-sequence
+// kernel for at most 128 keys, else the tiled kernel. A 16-bit problem that neither covers
+// (a (sequence, head) slice of 1 GiB or more) is refused, never sent to another kernel.
 aule_status_t dispatch(const aule::AttnProblem& p, aule_dtype_t dtype, hipStream_t stream) {
     aule::Dtype dt = static_cast<aule::Dtype>(dtype);
     hipError_t err;
-    if (!force_valu() && aule::short_supports(p, dt))
+    if (dt == aule::Dtype::F32)
+        err = aule::launch_attn_fwd_valu(p, dt, stream);
+    else if (aule::short_supports(p, dt))
         err = aule::launch_attn_fwd_short(p, dt, stream);
-    else if (!force_valu() && aule::mfma_supports(p, dt))
+    else if (aule::mfma_supports(p, dt))
         err = aule::launch_attn_fwd_mfma(p, dt, stream);
     else
-        err = aule::launch_attn_fwd_valu(p, dt, stream);
+        return fail(AULE_ERR_UNSUPPORTED, "fp16/bf16 slice too large for 32-bit offsets: one (%s, head) slice "
+                    "must span less than 1 GiB", p.cu_seqlens ? "sequence" : "batch");
     if (err != hipSuccess)
         return fail(AULE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     g_last_error[0] = '\0';
@@ -230,6 +224,8 @@ aule_status_t varlen_impl(const void* qkv, const int32_t* cu_seqlens, void* o, i
                           const VarlenMods& mods, hipStream_t stream) {
     if (total_tokens < 0 || max_seqlen < 0)
         return fail(AULE_ERR_INVALID_ARGUMENT, "total_tokens and max_seqlen must be >= 0");
+    if (total_tokens > 0 && max_seqlen == 0)
+        return fail(AULE_ERR_INVALID_ARGUMENT, "max_seqlen must be at least the longest sequence (got 0)");
     if (num_seqs <= 0)
         return fail(AULE_ERR_INVALID_ARGUMENT, "num_seqs must be positive (got %d)", num_seqs);
     if (heads <= 0)
@@ -269,10 +265,14 @@ aule_status_t varlen_impl(const void* qkv, const int32_t* cu_seqlens, void* o, i
     p.cu_seqlens = cu_seqlens;
     p.total_tokens = total_tokens;
     p.max_seqlen = max_seqlen;
-    // causal already hides every key after the query: only a left edge remains
-    const int32_t wr = causal ? -1 : mods.win_right;
-    p.mods = (mods.win_left >= 0 || wr >= 0 || mods.softcap > 0.f || mods.alibi) ? 1 : 0;
-    p.win_left = mods.win_left;
+    // causal already hides every key after the query: only a left edge remains. A window
+    // of max_seqlen keys or more masks nothing (no sequence is longer; the kernels clamp
+    // every sequence to max_seqlen), so it is unbounded: mapping it to -1 also keeps the
+    // kernels' row + window sums far from int32 overflow.
+    const int32_t wl = mods.win_left >= max_seqlen ? -1 : mods.win_left;
+    const int32_t wr = (causal || mods.win_right >= max_seqlen) ? -1 : mods.win_right;
+    p.mods = (wl >= 0 || wr >= 0 || mods.softcap > 0.f || mods.alibi) ? 1 : 0;
+    p.win_left = wl;
     p.win_right = wr;
     p.softcap = mods.softcap;
     p.alibi = mods.alibi;

@@ -364,3 +364,11 @@ SHORT_CONFIGS = {
     "s1_bf16_short_cross": ShortConfig("s1_bf16_short_cross", "bf16", 256, 12, 12, 64, 77, 64,
                                        False, seed=7),
 }
+
+# The packed-varlen benchmark harness of the ewbang.com article (its verification script's
+# comparison: batch 128, every sequence at the 4096-token maximum, 8 heads, head_dim 64,
+# fp16, non-causal): 524288 tokens, a 1.6 GB qkv pack.
+HARNESS_CONFIGS = {
+    "e1_f16_varlen_b128": VarlenConfig("e1_f16_varlen_b128", "f16", 128, 4096, 4096, 8, 64, False,
+                                       seed=8),
+}
