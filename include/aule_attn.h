@@ -186,6 +186,26 @@ size_t aule_attn_splitkv_workspace_size(int32_t batch, int32_t heads_q, int32_t 
                                         aule_dtype_t dtype, int32_t num_splits);
 
 /*
+ * aule_attn_fwd_splitkv without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. The split partials go to a fixed 32 MiB array inside the library, one per
+ * GPU, held from the library's first use on that GPU until the process ends; this call
+ * allocates nothing (no hipMalloc / hipFree, no allocating library routine).
+ *
+ * Arguments, operation, results and errors as aule_attn_fwd_splitkv (same split plan, same
+ * kernels: the outputs are identical), without workspace / workspace_bytes. A problem whose
+ * partials need more than 32 MiB (aule_attn_splitkv_workspace_size(...) > 33554432) is
+ * AULE_ERR_UNSUPPORTED, nothing launched. Every call on a GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.
+ */
+aule_status_t aule_attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                            int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                            int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                            int32_t causal, float scale, aule_dtype_t dtype,
+                                            int32_t num_splits, hipStream_t stream);
+
+/*
  * Attention forward that also writes the per-row log-sum-exp needed by the backward.
  *
  * Same operation, arguments and rules as aule_attn_fwd, plus

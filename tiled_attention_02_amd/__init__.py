@@ -45,8 +45,8 @@ AULE_OK, AULE_ERR_INVALID_ARGUMENT, AULE_ERR_UNSUPPORTED, AULE_ERR_HIP = 0, 1, 2
 
 EXPORTED = ("aule_attn_fwd", "aule_attn_fwd_lse", "aule_attn_bwd", "aule_attn_fwd_varlen",
             "aule_attn_fwd_varlen_mods",
-            "aule_attn_fwd_splitkv", "aule_attn_splitkv_workspace_size", "aule_status_string",
-            "aule_last_error")
+            "aule_attn_fwd_splitkv", "aule_attn_splitkv_workspace_size",
+            "aule_attn_fwd_splitkv_noalloc", "aule_status_string", "aule_last_error")
 
 _lib = None
 
@@ -86,6 +86,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.aule_attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32,
                                           ctypes.c_int, i32, vp, ctypes.c_size_t, vp]
     lib.aule_attn_fwd_splitkv.restype = ctypes.c_int
+    lib.aule_attn_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                                  i32, f32, ctypes.c_int, i32, vp]
+    lib.aule_attn_fwd_splitkv_noalloc.restype = ctypes.c_int
     lib.aule_attn_splitkv_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.c_int, i32]
     lib.aule_attn_splitkv_workspace_size.restype = ctypes.c_size_t
     lib.aule_status_string.argtypes = [ctypes.c_int]
@@ -148,6 +151,16 @@ def aule_attn_fwd_splitkv(q, k, v, o, batch, heads_q, heads_kv, seqlen_q, seqlen
                                                 seqlen_k, head_dim, int(causal), float(scale),
                                                 int(dtype), int(num_splits), workspace,
                                                 int(workspace_bytes), stream)
+
+
+def aule_attn_fwd_splitkv_noalloc(q, k, v, o, batch, heads_q, heads_kv, seqlen_q, seqlen_k,
+                                  head_dim, causal, scale, dtype, num_splits, stream=0) -> int:
+    """Raw call: device pointers as ints; the split partials live in the library's own
+    device array (nothing is allocated); returns the status code."""
+    return load_library().aule_attn_fwd_splitkv_noalloc(q, k, v, o, batch, heads_q, heads_kv,
+                                                        seqlen_q, seqlen_k, head_dim, int(causal),
+                                                        float(scale), int(dtype), int(num_splits),
+                                                        stream)
 
 
 def aule_attn_splitkv_workspace_size(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
@@ -429,7 +442,7 @@ def flash_attn_varlen_qkvpacked_func(qkv, cu_seqlens, max_seqlen, dropout_p=0.0,
 
 __all__ = ["aule_attn_fwd", "aule_attn_fwd_lse", "aule_attn_bwd", "aule_attn_fwd_varlen",
            "aule_attn_fwd_varlen_mods",
-           "aule_attn_fwd_splitkv", "flash_attention_backward",
+           "aule_attn_fwd_splitkv", "aule_attn_fwd_splitkv_noalloc", "flash_attention_backward",
            "aule_attn_splitkv_workspace_size", "aule_status_string", "aule_last_error",
            "flash_attention", "flash_attention_decode", "flash_attn_varlen_qkvpacked_func",
            "load_library", "AuleError", "LIB_PATH", "EXPORTED"]

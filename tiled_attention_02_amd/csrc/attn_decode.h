@@ -37,5 +37,9 @@ struct DecodeProblem {
 int decode_keys_per_tile(Dtype dt);
 // Launches the partial kernel and the merge kernel on `stream`; does not synchronise.
 hipError_t launch_attn_decode(const DecodeProblem& p, Dtype dt, hipStream_t stream);
+// The fixed device workspace of the no-allocation entry point: its size, and its address on
+// the current device (looked up once per device).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** ptr);
 
 }  // namespace aule

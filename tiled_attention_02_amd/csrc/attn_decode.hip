@@ -31,6 +31,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "attn_decode.h"
 
 namespace aule {
@@ -446,6 +448,37 @@ hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Workspace of the entry point that allocates nothing: one fixed array per GPU, held from
+// the library's first use on that GPU until the process ends. Every call on a GPU shares
+// it, so calls that overlap in time on one GPU race. Nothing in it needs clearing: the
+// partial kernel writes every (split, row) slot that the merge kernel reads.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** ptr) {
+    // In host code `scratch` only names the symbol; the array's address on the current
+    // device comes from the runtime, once per device, and is what the kernels are given.
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!a) return hipErrorInvalidSymbol;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 int decode_keys_per_tile(Dtype dt) { return dt == Dtype::F32 ? 32 : 64; }
 

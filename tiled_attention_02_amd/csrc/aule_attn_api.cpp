@@ -421,12 +421,17 @@ aule_status_t aule_attn_fwd_varlen_mods(const void* qkv, const int32_t* cu_seqle
                        causal, scale, dtype, m, stream);
 }
 
-aule_status_t aule_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
-                                    int32_t batch, int32_t heads_q, int32_t heads_kv,
-                                    int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
-                                    int32_t causal, float scale, aule_dtype_t dtype,
-                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared by both split-KV entry points: validate, plan the splits, place the partials in
+// `workspace` (the caller's buffer, or the library's device array when `own` is set), launch.
+aule_status_t splitkv_impl(const void* q, const void* k, const void* v, void* o, int32_t batch,
+                           int32_t heads_q, int32_t heads_kv, int32_t seqlen_q, int32_t seqlen_k,
+                           int32_t head_dim, int32_t causal, float scale, aule_dtype_t dtype,
+                           int32_t num_splits, void* workspace, size_t workspace_bytes, bool own,
+                           hipStream_t stream) {
     if (aule_status_t st = check_splitkv(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim,
                                          causal, dtype, num_splits))
         return st;
@@ -436,12 +441,16 @@ aule_status_t aule_attn_fwd_splitkv(const void* q, const void* k, const void* v,
         g_last_error[0] = '\0';
         return AULE_OK;  // empty problem
     }
-    if (!q || !k || !v || !o || !workspace)
+    if (!q || !k || !v || !o || (!own && !workspace))
         return fail(AULE_ERR_INVALID_ARGUMENT, "null pointer");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(workspace))
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (!own && !aligned16(workspace)))
         return fail(AULE_ERR_INVALID_ARGUMENT, "tensor and workspace pointers must be 16-byte aligned");
     const SplitPlan pl = plan_splits(batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, dtype, num_splits);
-    if (workspace_bytes < pl.bytes)
+    if (own && pl.bytes > aule::decode_scratch_bytes())
+        return fail(AULE_ERR_UNSUPPORTED, "the split partials need %zu bytes; the library's device array "
+                    "holds %zu (use aule_attn_fwd_splitkv with a workspace, or fewer splits)",
+                    pl.bytes, aule::decode_scratch_bytes());
+    if (!own && workspace_bytes < pl.bytes)
         return fail(AULE_ERR_INVALID_ARGUMENT, "workspace of %zu bytes is smaller than the %zu needed",
                     workspace_bytes, pl.bytes);
     const size_t es = elem_size(dtype);
@@ -449,9 +458,14 @@ aule_status_t aule_attn_fwd_splitkv(const void* q, const void* k, const void* v,
     const size_t nkv = (size_t)batch * heads_kv * seqlen_k * head_dim * es;
     if (overlaps(o, nq, q, nq) || overlaps(o, nq, k, nkv) || overlaps(o, nq, v, nkv))
         return fail(AULE_ERR_INVALID_ARGUMENT, "output overlaps an input");
-    if (overlaps(workspace, pl.bytes, q, nq) || overlaps(workspace, pl.bytes, k, nkv) ||
-        overlaps(workspace, pl.bytes, v, nkv) || overlaps(workspace, pl.bytes, o, nq))
+    if (!own && (overlaps(workspace, pl.bytes, q, nq) || overlaps(workspace, pl.bytes, k, nkv) ||
+                 overlaps(workspace, pl.bytes, v, nkv) || overlaps(workspace, pl.bytes, o, nq)))
         return fail(AULE_ERR_INVALID_ARGUMENT, "workspace overlaps a tensor");
+    if (own) {
+        const hipError_t e = aule::decode_scratch(&workspace);
+        if (e != hipSuccess)
+            return fail(AULE_ERR_HIP, "device workspace lookup failed: %s", hipGetErrorString(e));
+    }
 
     aule::DecodeProblem p{};
     p.q = q; p.k = k; p.v = v; p.o = o;
@@ -468,6 +482,29 @@ aule_status_t aule_attn_fwd_splitkv(const void* q, const void* k, const void* v,
         return fail(AULE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(err));
     g_last_error[0] = '\0';
     return AULE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+aule_status_t aule_attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                                    int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                    int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                    int32_t causal, float scale, aule_dtype_t dtype,
+                                    int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    return splitkv_impl(q, k, v, o, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, causal,
+                        scale, dtype, num_splits, workspace, workspace_bytes, false, stream);
+}
+
+aule_status_t aule_attn_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
+                                            int32_t batch, int32_t heads_q, int32_t heads_kv,
+                                            int32_t seqlen_q, int32_t seqlen_k, int32_t head_dim,
+                                            int32_t causal, float scale, aule_dtype_t dtype,
+                                            int32_t num_splits, hipStream_t stream) {
+    return splitkv_impl(q, k, v, o, batch, heads_q, heads_kv, seqlen_q, seqlen_k, head_dim, causal,
+                        scale, dtype, num_splits, nullptr, 0, true, stream);
 }
 
 size_t aule_attn_splitkv_workspace_size(int32_t batch, int32_t heads_q, int32_t heads_kv,
