@@ -169,21 +169,50 @@ def make_step(cfg, dev_inputs, torch):
                                                          causal=cfg.causal, out=out, **mods)
 
 
-def time_steps(step, steps, warmup, torch):
+def time_steps(step, steps, warmup, torch, per_launch=False):
+    """Wall-clock seconds per step and HIP-event seconds per step over exactly `steps` timed
+    steps after `warmup` untimed ones. With `per_launch`, an event pair around every step (on
+    the launch stream) also gives the per-launch durations (sorted, seconds)."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()          # the stream the kernels are launched on
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)] if per_launch else None
     t0 = time.perf_counter()
     ev0.record(stream)
-    for _ in range(steps):
+    for i in range(steps):
+        if marks:
+            marks[i].record(stream)
         step()
+    if marks:
+        marks[steps].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall / steps, ev0.elapsed_time(ev1) / 1e3 / steps
+    launches = sorted(marks[i].elapsed_time(marks[i + 1]) / 1e3 for i in range(steps)) if marks else None
+    return wall / steps, ev0.elapsed_time(ev1) / 1e3 / steps, launches
+
+
+def cold_median(step, launches, torch, scrub_mib=512):
+    """Median seconds of `launches` event-timed launches, each after a write of scrub_mib MiB
+    that evicts the caches (the 256 MB Infinity Cache included)."""
+    scrub = torch.empty(scrub_mib << 20, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    for _ in range(launches):
+        scrub.fill_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / 1e3)
+    del scrub
+    times.sort()
+    return times[len(times) // 2]
 
 
 def cpu_baseline(cfg, host_inputs, budget_s):
@@ -287,6 +316,31 @@ def cpu_baseline(cfg, host_inputs, budget_s):
     G = cfg.heads_q // cfg.heads_kv
     n = cfg.seqlen
     pairs = n * (n + 1) // 2 if cfg.causal else n * n
+    if n * n * 8 > (1 << 30):
+        # a whole slice's fp64 score matrix would pass 1 GiB (8.6 GB at 32k tokens): the
+        # oracle computes the sampled query rows of every head instead, and the full problem's
+        # time is extrapolated from the sampled (query, key) pairs
+        from workloads import sampled_rows
+        rows = sampled_rows(n)
+        sp = int(sum(r + 1 for r in rows)) if cfg.causal else rows.size * n
+        t0 = time.perf_counter()
+        heads = 0
+        for b in range(cfg.batch):
+            for hq in range(cfg.heads_q):
+                hk = hq // G
+                oracle.attention_ref_rows(q[b:b + 1, hq:hq + 1], k[b:b + 1, hk:hk + 1],
+                                          v[b:b + 1, hk:hk + 1], rows, causal=cfg.causal,
+                                          scale=cfg.softmax_scale)
+                heads += 1
+        dt = time.perf_counter() - t0
+        sampled_pairs = sp * heads
+        full_pairs = pairs * cfg.batch * cfg.heads_q
+        return {"value": 4 * cfg.head_dim * sampled_pairs / dt / 1e12, "unit": "TFLOP/s",
+                "cores": threads, "kind": "oracle",
+                "sample": f"{rows.size} sampled query rows of each of {heads} (batch, query head) "
+                f"slices, {dt:.1f} s",
+                "extrapolated_full_s": round(dt * full_pairs / sampled_pairs, 1),
+                "extrapolation": "sampled time x full pairs / sampled pairs (label only)"}
     t0 = time.perf_counter()
     heads = 0
     for b in range(cfg.batch):
@@ -319,7 +373,9 @@ def main():
     import torch
     from workloads import (BWD_CONFIGS, CONFIGS, DECODE_CONFIGS, MODS_CONFIGS, SHORT_CONFIGS,
                            BwdConfig, DecodeConfig, ModsConfig, ShortConfig)
-    ALL = {**CONFIGS, **DECODE_CONFIGS, **BWD_CONFIGS, **MODS_CONFIGS, **SHORT_CONFIGS}
+    from workloads import HARNESS_CONFIGS
+    ALL = {**CONFIGS, **DECODE_CONFIGS, **BWD_CONFIGS, **MODS_CONFIGS, **SHORT_CONFIGS,
+           **HARNESS_CONFIGS}
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
@@ -334,7 +390,7 @@ def main():
     cfg = ALL[args.workload]
     dev_in, host_in = device_inputs(cfg, torch)
     step = make_step(cfg, dev_in, torch)
-    wall_s, kern_s = time_steps(step, args.steps, args.warmup, torch)
+    wall_s, kern_s, launches = time_steps(step, args.steps, args.warmup, torch, per_launch=True)
 
     flops = cfg.flops()
     value = flops / wall_s / 1e12
@@ -358,9 +414,20 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(cfg.name),
                      "kernel_ms": round(kern_s * 1e3, 4),
+                     "launch_ms": {"median": round(launches[len(launches) // 2] * 1e3, 4),
+                                   "min": round(launches[0] * 1e3, 4),
+                                   "max": round(launches[-1] * 1e3, 4)},
                      "algorithmic_flops_per_launch": flops,
                      "algorithmic_bytes_per_launch": cfg.bytes_compulsory()},
     }
+    if hasattr(cfg, "pairs") and not isinstance(cfg, (DecodeConfig, ShortConfig)):
+        # the exact unmasked-pair count, and the common convention that counts a causal
+        # problem as half of the full square (B * N^2 / 2 pairs)
+        line["config"]["flops_exact"] = flops
+        half = half_convention_flops(cfg)
+        if half is not None:
+            line["config"]["flops_half_convention"] = half
+            line["config"]["value_half_convention"] = round(half / wall_s / 1e12, 2)
     if isinstance(cfg, ModsConfig):
         line["metric"] = "attention varlen fwd with window/softcap/ALiBi TFLOPS (visible pairs) and % of MI355X bf16 MFMA peak"
     if isinstance(cfg, BwdConfig):
@@ -385,17 +452,37 @@ def main():
             if name == cfg.name:
                 continue
             di, _ = device_inputs(c, torch)
-            w, kt = time_steps(make_step(c, di, torch), max(5, args.steps // 5), 3, torch)
+            st = make_step(c, di, torch)
+            # the pages' harness method: 20 warm-ups, then 100 launches, the median reported
+            n = 100 if c.flops() < 1e12 else 20
+            _, kt, ls = time_steps(st, n, 20, torch, per_launch=True)
+            med = ls[len(ls) // 2]
+            cold = cold_median(st, 21, torch)
             pk = MFMA_PEAK_TFLOPS[c.dtype]
-            gbs = c.bytes_compulsory() / kt / 1e9
-            print(f"[bench] {name}: {kt * 1e3:.4f} ms/launch, {c.flops() / kt / 1e12:.1f} TFLOP/s "
-                  f"({100 * c.flops() / kt / 1e12 / pk:.1f}% of {pk:.0f}), "
+            gbs = c.bytes_compulsory() / med / 1e9
+            print(f"[bench] {name}: median {med * 1e3:.4f} ms/launch (mean {kt * 1e3:.4f}, cold-cache "
+                  f"median {cold * 1e3:.4f}), {c.flops() / med / 1e12:.1f} TFLOP/s "
+                  f"({100 * c.flops() / med / 1e12 / pk:.1f}% of {pk:.0f}), "
                   f"{gbs:.0f} GB/s compulsory ({100 * gbs / HBM_PEAK_GBS:.1f}% of 8 TB/s)", file=sys.stderr)
             del di
             torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, host_in, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def half_convention_flops(cfg):
+    """FLOPs with a causal problem counted as half the full square (4*d*Hq*B*N^2/2), the
+    figure many reports quote; None for the workloads it does not apply to."""
+    from workloads import BwdConfig, DenseConfig, ModsConfig, VarlenConfig
+    if isinstance(cfg, ModsConfig) or not getattr(cfg, "causal", False):
+        return None
+    per_pair = 10 if isinstance(cfg, BwdConfig) else 4
+    if isinstance(cfg, DenseConfig):
+        return per_pair * cfg.head_dim * cfg.heads_q * cfg.batch * cfg.seqlen * cfg.seqlen // 2
+    if isinstance(cfg, VarlenConfig):
+        return per_pair * cfg.head_dim * cfg.heads * sum(int(l) ** 2 for l in cfg.lengths()) // 2
+    return None
 
 
 def describe(cfg):

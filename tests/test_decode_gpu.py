@@ -1,6 +1,6 @@
 """GPU parity of the split-KV decoding path (aule_attn_fwd_splitkv, through the C-ABI
 library) against the CPU fp64 oracle's attention_ref_decode on the same seeded,
-dtype-rounded inputs. Bars as for the forward: 1e-5 fp32 (scaled with |scale|*sqrt(d)),
+dtype-rounded inputs. Bars as for the forward: 1e-5 fp32,
 2e-3 fp16, 1e-2 bf16, max abs error over every element."""
 import math
 

@@ -441,6 +441,18 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
             }
         }
     };
+    // Whether any of this wave's query rows sees a key of sub-step `sub` (wave-uniform).
+    auto wave_sees = [&](int sub) -> bool {
+        const int k0 = cur.kb0 + 32 * sub;
+        const int qlo = cur.qr0, qhi = cur.qr0 + 32 * NB - 1;
+        if (qlo >= cur.Lq) return false;
+        if (CAUSAL && k0 > qhi) return false;
+        if constexpr (MODS) {
+            if (p.win_left >= 0 && k0 + 31 < qlo - p.win_left) return false;
+            if (!CAUSAL && p.win_right >= 0 && k0 > qhi + p.win_right) return false;
+        }
+        return true;
+    };
     // V^T fragments of sub-step `sub` (A operands of O^T = V^T P^T): two transposed 8-byte
     // reads per 16-key chunk and 32-row d-block
     auto load_v = [&](int sub, const u32x4* cV, const LaneAddr& la, u32x4 (&vf)[2][DB]) {
@@ -638,17 +650,27 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                 for (int hh = 0; hh < SPT; ++hh) {
                     const int i = SPT * t + hh;
                     if (i >= cur.nsub) break;
-                    mma_qk(kf, s_cur);
+                    // varlen and score-modifier problems: a sub-step none of this wave's rows
+                    // can see (a causal or window edge of the workgroup's other rows, or rows
+                    // past the sequence) only does its share of the tile copy and the next
+                    // fragment reads (measured: -5% time on the bf16 modifier workload, -3% on the
+                    // bf16 varlen one). Not for dense problems: the persistent form's 64-row
+                    // items leave one such sub-step to half of the waves and the branch costs it
+                    // 17 registers; on the fp16 head_dim-64 causal workload it measured +3%.
+                    const bool live = !VARLEN || wave_sees(i);
+                    if (live) mma_qk(kf, s_cur);
                     if (hh < DMA_PARTS && copy_next)
                         issue_tile_part<NI, DMA_PARTS>(hh, cur.rk, cur.rv, koff, voff, (t + AHEAD) * tk, (t + AHEAD) * tv,
                                                        lK[bn], lV[bn], wave);
-                    load_v(i, cVb[b], la, vf);
+                    if (live) load_v(i, cVb[b], la, vf);
                     if (hh + 1 < SPT) load_k(i + 1, cKb[b], la, kf);
-                    mask(i, s_cur);
-                    Soft st;
-                    softmax(s_cur, p_cur, st);
-                    finish(st);
-                    mma_pv(vf, p_cur);
+                    if (live) {
+                        mask(i, s_cur);
+                        Soft st;
+                        softmax(s_cur, p_cur, st);
+                        finish(st);
+                        mma_pv(vf, p_cur);
+                    }
                 }
             }
         }
