@@ -91,11 +91,11 @@ __device__ __forceinline__ void put_rows(char* tile, const u32x4 (&c)[(Tile<D, N
 }
 
 // A operand with rows in sigma order from a ROWS tile: lane l supplies row sigma(l % 32),
-// k-chunk 2ks + h (stored at chunk (2ks + h) ^ kswz(sigma(l % 32)) = (2ks + h) ^ (l % 32 % KC)).
+// k-chunk 2ks + h (stored at chunk (2ks + h) ^ kswz(sigma(l % 32)) = (2ks + h) ^ kx_lane(l % 32)).
 template <int D, int L = ROWS>
 __device__ __forceinline__ u32x4 rd_rows(const char* tile, int ks, int lane) {
     const int l32 = lane & 31;
-    const int x = L == PAD ? 0 : (l32 & (Tile<D>::CPR - 1));
+    const int x = L == PAD ? 0 : kx_lane<Tile<D>::CPR>(l32);
     return *reinterpret_cast<const u32x4*>(tile + sigma(l32) * row_bytes<D, L>() + (((2 * ks + (lane >> 5)) ^ x) * 16));
 }
 // A operand of a transposed COLS tile: A[m = column 32db + l % 32][k = row 16kk + 8h .. + 7],

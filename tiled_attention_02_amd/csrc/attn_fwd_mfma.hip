@@ -360,7 +360,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         LaneAddr a;
         const int l32 = ln_raw & 31, tg = ln_raw >> 4, tc = ln_raw & 15;
         a.krow_sig = sigma(l32);
-        a.kx = l32 & (KC - 1);
+        a.kx = kx_lane<KC>(l32);
         a.h = ln_raw >> 5;
         a.tv_key = 8 * (tg >> 1) + (tc >> 2);          // + 16*kc + 4*t
         a.tv_chunk = 2 * (tg & 1) + ((tc & 3) >> 1);   // + 4*db

@@ -86,7 +86,7 @@ void attn_fwd_short_kernel(AttnProblem p, int n_rb) {
     }
 
     // per-lane LDS address terms of the fragment reads
-    const int krow_sig = sigma(ln), kx = ln & (KC - 1);
+    const int krow_sig = sigma(ln), kx = kx_lane<KC>(ln);
     const int tg = lane >> 4, tc = lane & 15;
     const int tv_key = 8 * (tg >> 1) + (tc >> 2);
     const int tv_chunk = 2 * (tg & 1) + ((tc & 3) >> 1);

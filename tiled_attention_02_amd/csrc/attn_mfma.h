@@ -78,10 +78,19 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // 16-byte chunk swizzles (XOR on the chunk index inside a row) of K and V tiles in LDS.
 // K rows: the S^T reads of one instruction hit rows sigma(0..31) at one column; chunk c of
-//   row r sits at c ^ (sigma(r % 32) % KC), so those reads spread over distinct chunks.
+//   row r sits at c ^ kswz(r) with kswz(r) = kx_lane(sigma(r % 32)), the mask of the lane
+//   that reads row r (sigma is an involution). Each group of 16 lanes (one 256-byte pass of
+//   the LDS banks) must hit 16 distinct 16-byte slots: with 16 chunks per row (256-byte rows)
+//   kx_lane(l) = l % 16 does that; with 8 chunks (128-byte rows, two rows per bank row) the
+//   row's parity (l % 2, which sigma keeps) picks the half and kx_lane(l) = (l / 2) % 8 the
+//   chunk (l % 8 there left lanes l and l + 8 on one slot: 2-way conflicts).
 // V rows: a transposed read touches 4 consecutive rows x 2 (or 4) neighbouring chunks; the
 //   per-row XOR masks below make those slots distinct modulo 8 and modulo 16 chunks.
-template <int KC> __device__ __forceinline__ int kswz(int row) { return sigma(row & 31) & (KC - 1); }
+template <int KC> __device__ __forceinline__ int kx_lane(int l32) {
+    static_assert(KC == 8 || KC == 16, "rows of 8 or 16 chunks");
+    return KC == 16 ? (l32 & 15) : ((l32 >> 1) & 7);
+}
+template <int KC> __device__ __forceinline__ int kswz(int row) { return kx_lane<KC>(sigma(row & 31)); }
 template <int KC> __device__ __forceinline__ int vswz(int row) {
     if constexpr (KC == 16) return (0xCA60 >> (4 * (row & 3))) & 15;   // 0, 6, 10, 12
     else return 2 * (row & 3);
