@@ -646,6 +646,12 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                 u32x4 kf[KS];
                 u32x4 vf[2][DB];
                 load_k(SPT * t, cKb[b], la, kf);
+                // All K fragment reads of the tile's first sub-step are issued before its first
+                // product: left to itself the scheduler chains them through one register quad,
+                // read -> wait -> product, eight LDS round trips in a row after every barrier
+                // (measured: -5% time on the fp16 head_dim-64 causal workload, -1% on the bf16
+                // GQA ones, outputs bitwise unchanged).
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int hh = 0; hh < SPT; ++hh) {
                     const int i = SPT * t + hh;
