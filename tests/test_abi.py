@@ -238,6 +238,17 @@ def test_bwd_rejects_invalid_arguments(lib, kw, status):
     assert aule.aule_last_error() != ""
 
 
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_bwd_oversized_16bit_slices_are_refused(lib, dtype):
+    """The backward's matrix-core kernels address one (batch, head) slice with 32-bit buffer
+    offsets: a 16-bit slice of 1 GiB or more is refused before any launch."""
+    big = dict(q=BIG["q"], k=BIG["k"], v=BIG["v"], o=BIG["o"], do=0x700000000000,
+               lse=0x800000000000, dq=0x900000000000, dk=0xA00000000000, dv=0xB00000000000)
+    st = bwd(**big, heads_q=1, heads_kv=1, seqlen_q=4_200_000, seqlen_k=4_200_000, head_dim=128,
+             causal=0, dtype=dtype)
+    assert st == UNS and "1 GiB" in aule.aule_last_error()
+
+
 def test_fwd_lse_rejects_null_lse(lib):
     st = aule.aule_attn_fwd_lse(P["q"], P["k"], P["v"], P["o"], None, 1, 4, 2, 16, 16, 64, 1,
                                 0.125, BF16, None)

@@ -25,6 +25,8 @@
 // passes store each staged tile XOR-swizzled in the layout of the read that uses it.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "attn_bwd.h"
 #include "attn_mfma.h"
 
@@ -52,18 +54,26 @@ struct Tile {
     static_assert(NCH >= 1 && NCH * NT == 32 * CPR, "tile chunks must split evenly");
 };
 
-// Rows [r0, r0 + 32) of a [rows, d] slice as 16-byte chunks, this thread's share (zero past
-// the last row and past head_dim).
+// Rows [r0, r0 + 32) of a [rows, d] slice as 16-byte chunks, this thread's share, through a
+// buffer resource covering exactly the slice: rows past the end read as zero (the hardware's
+// range check) and chunks past head_dim are sent past the range, so there is no branch and no
+// zero fill (with those, the compiler waited for every load in flight before refilling a
+// staging set, which undid the two-deep staging).
 template <typename T, int D, int NT = kThreads>
-__device__ __forceinline__ void fetch_rows(u32x4 (&c)[(Tile<D, NT>::NCH)], const T* base, int r0, int rows, int d) {
+__device__ __forceinline__ void fetch_rows_buf(u32x4 (&c)[(Tile<D, NT>::NCH)], __amdgpu_buffer_rsrc_t rs, int r0, int d) {
 #pragma unroll
     for (int i = 0; i < Tile<D, NT>::NCH; ++i) {
         const int idx = (int)threadIdx.x + NT * i;
         const int row = idx / Tile<D>::CPR, ch = idx % Tile<D>::CPR;
-        const int r = r0 + row;
-        c[i] = (r < rows && ch * 8 < d) ? *reinterpret_cast<const u32x4*>(base + (int64_t)r * d + ch * 8)
-                                        : u32x4{0u, 0u, 0u, 0u};
+        const uint32_t off = ch * 8 < d ? (uint32_t)(r0 + row) * (uint32_t)(d * (int)sizeof(T)) + (uint32_t)ch * 16u : kOobOffset;
+        c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
     }
+}
+// Resource for a [rows, d] slice of T (at most 1 GiB, checked by the host).
+template <typename T>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const T* base, int rows, int d) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, rows > 0 ? rows * d * (int)sizeof(T) : 0,
+                                             (int)kBufferFlags);
 }
 // Two LDS layouts of a 32-row tile, one per read pattern, with the XOR swizzles of the
 // forward kernel's K and V tiles (chunk c of row r stored at chunk c ^ swz(r)):
@@ -212,14 +222,19 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
         const int g = it / ntile, i0 = i_start + QR * (it - g * ntile);
         const int64_t bh = (int64_t)b * p.heads_q + hk * G + g;
         const int64_t q_off = bh * Nq * d;
+        const __amdgpu_buffer_rsrc_t rq = slice_rsrc(static_cast<const T*>(p.q) + q_off, Nq, d);
+        const __amdgpu_buffer_rsrc_t rdo = slice_rsrc(static_cast<const T*>(p.do_) + q_off, Nq, d);
 #pragma unroll
         for (int hf = 0; hf < QH; ++hf) {
-            fetch_rows<T, D, NT>(st.q[hf], static_cast<const T*>(p.q) + q_off, i0 + 32 * hf, Nq, d);
-            fetch_rows<T, D, NT>(st.dO[hf], static_cast<const T*>(p.do_) + q_off, i0 + 32 * hf, Nq, d);
-            if constexpr (PASS == 1) fetch_rows<T, D, NT>(st.o[hf], static_cast<const T*>(p.o) + q_off, i0 + 32 * hf, Nq, d);
+            fetch_rows_buf<T, D, NT>(st.q[hf], rq, i0 + 32 * hf, d);
+            fetch_rows_buf<T, D, NT>(st.dO[hf], rdo, i0 + 32 * hf, d);
+            if constexpr (PASS == 1)
+                fetch_rows_buf<T, D, NT>(st.o[hf], slice_rsrc(static_cast<const T*>(p.o) + q_off, Nq, d), i0 + 32 * hf, d);
         }
-        const int r = i0 + (int)threadIdx.x;
-        st.lse = ((int)threadIdx.x < QR && r < Nq) ? p.lse[bh * Nq + r] : 0.f;
+        // every thread loads (rows past the end read as zero); the first QR are committed
+        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.lse) + bh * Nq, (short)0, Nq * 4, (int)kBufferFlags);
+        const uint32_t loff = (int)threadIdx.x < QR ? (uint32_t)(i0 + (int)threadIdx.x) * 4u : kOobOffset;
+        st.lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (int)loff, 0, 0));
     };
     auto commit = [&](int buf, const Stage& st) {
 #pragma unroll
@@ -238,7 +253,7 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
 #pragma unroll
                 for (int off = 1; off < TL::CPR; off <<= 1) x += __shfl_xor(x, off);
                 const int idx = (int)threadIdx.x + NT * i;
-                if (idx % TL::CPR == 0) sD[buf][32 * hf + idx / TL::CPR] = x;
+                if (idx % TL::CPR == 0) sD[buf][32 * hf + idx / TL::CPR] = -x;   // -D
             }
         }
         if ((int)threadIdx.x < QR) sL[buf][threadIdx.x] = st.lse * kLog2eF;
@@ -252,35 +267,63 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
 #pragma unroll
         for (int hf = 0; hf < QH; ++hf) {
         const int i0 = i0q + 32 * hf;
-        // S = Q K^T, dP = dO V^T: register r holds query i0 + 16(r/8) + 8h + r%8, key `key`
+        // S = Q K^T, dP - D = dO V^T - D: register r holds query i0 + 16(r/8) + 8h + r%8, key
+        // `key`; the dP accumulator starts from -D of its rows (two runs of 8 consecutive rows,
+        // 16-byte reads), so dS = P (dP - D) needs no further registers
         f32x16 s = f32x16{}, dp = f32x16{};
+        if constexpr (PASS == 1) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const float4* pd = reinterpret_cast<const float4*>(&sD[buf][32 * hf + 16 * kk + 8 * h]);
+                const float4 x = pd[0], y = pd[1];
+                dp[8 * kk + 0] = x.x; dp[8 * kk + 1] = x.y; dp[8 * kk + 2] = x.z; dp[8 * kk + 3] = x.w;
+                dp[8 * kk + 4] = y.x; dp[8 * kk + 5] = y.y; dp[8 * kk + 6] = y.z; dp[8 * kk + 7] = y.w;
+            }
+        }
 #pragma unroll
         for (int ks = 0; ks < TL::KS; ++ks) {
             s = Mfma<T>::mma(rd_rows<D>(sQ[buf][hf], ks, lane), kf[ks], s);
             if constexpr (PASS == 1) dp = Mfma<T>::mma(rd_rows<D>(sdO[buf][hf], ks, lane), vf[ks], dp);
         }
-        // tiles away from the diagonal and the ends need no mask (a uniform branch)
-        const bool inner = i0 + 32 <= Nq && kw0 + 32 <= Nk && (!p.causal || kw0 + 31 <= i0);
+        // P (and dS) packed to 16 bit. The row statistics of each run of 8 consecutive query
+        // rows are read as two 16-byte vectors. Tiles away from the diagonal and the ends need
+        // no mask: a uniform branch picks the mask-free form; on edge tiles every exponential
+        // is taken and masked pairs are selected to 0 (no per-element branch).
         u32x4 pf[2], dsf[2];
+        auto p_ds = [&](auto masked) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            const int q0 = 16 * kk + 8 * h;
-            float pv[8], dsv[8];
+            for (int kk = 0; kk < 2; ++kk) {
+                const int q0 = 16 * kk + 8 * h;
+                float lq[8];
+                {
+                    const float4* pl = reinterpret_cast<const float4*>(&sL[buf][32 * hf + q0]);
+                    const float4 a = pl[0], c = pl[1];
+                    lq[0] = a.x; lq[1] = a.y; lq[2] = a.z; lq[3] = a.w;
+                    lq[4] = c.x; lq[5] = c.y; lq[6] = c.z; lq[7] = c.w;
+                }
+                float pv[8], dsv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int qi = i0 + q0 + e;
-                const bool vis = inner || (qi < Nq && key < Nk && (!p.causal || key <= qi));
-                const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -sL[buf][32 * hf + q0 + e])) : 0.f;
-                pv[e] = pe;
-                dsv[e] = PASS == 1 ? pe * (dp[8 * kk + e] - sD[buf][32 * hf + q0 + e]) : 0.f;
+                for (int e = 0; e < 8; ++e) {
+                    float pe = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -lq[e]));
+                    if constexpr (decltype(masked)::value) {
+                        const int qi = i0 + q0 + e;
+                        const bool vis = qi < Nq && key < Nk && (!p.causal || key <= qi);
+                        pe = vis ? pe : 0.f;
+                    }
+                    pv[e] = pe;
+                    dsv[e] = PASS == 1 ? pe * dp[8 * kk + e] : 0.f;
+                }
+                if constexpr (PASS == 0)
+                    pf[kk] = u32x4{Mfma<T>::pack2(pv[0], pv[1]), Mfma<T>::pack2(pv[2], pv[3]),
+                                   Mfma<T>::pack2(pv[4], pv[5]), Mfma<T>::pack2(pv[6], pv[7])};
+                else
+                    dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
+                                    Mfma<T>::pack2(dsv[4], dsv[5]), Mfma<T>::pack2(dsv[6], dsv[7])};
             }
-            if constexpr (PASS == 0)
-                pf[kk] = u32x4{Mfma<T>::pack2(pv[0], pv[1]), Mfma<T>::pack2(pv[2], pv[3]),
-                               Mfma<T>::pack2(pv[4], pv[5]), Mfma<T>::pack2(pv[6], pv[7])};
-            else
-                dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
-                            Mfma<T>::pack2(dsv[4], dsv[5]), Mfma<T>::pack2(dsv[6], dsv[7])};
-        }
+        };
+        const bool inner = i0 + 32 <= Nq && kw0 + 32 <= Nk && (!p.causal || kw0 + 31 <= i0);
+        if (inner) p_ds(std::false_type{});
+        else p_ds(std::true_type{});
         // dV^T += dO^T P (PASS 0) or dK^T += Q^T dS (PASS 1)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
@@ -369,9 +412,10 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
     // two register staging sets, as in the dK / dV kernel: key tile t + 2 is fetched while
     // tile t + 1 (fetched an iteration earlier) is committed to LDS
     struct Stage { u32x4 k[TL::NCH], v[TL::NCH]; };
+    const __amdgpu_buffer_rsrc_t rk = slice_rsrc(Kb, Nk, d), rv = slice_rsrc(Vb, Nk, d);
     auto fetch = [&](int t, Stage& st) {
-        fetch_rows<T, D>(st.k, Kb, 32 * t, Nk, d);
-        fetch_rows<T, D>(st.v, Vb, 32 * t, Nk, d);
+        fetch_rows_buf<T, D>(st.k, rk, 32 * t, d);
+        fetch_rows_buf<T, D>(st.v, rv, 32 * t, d);
     };
     auto commit = [&](int buf, const Stage& st) {
         put_rows<D, PAD>(sK[buf], st.k);
@@ -388,22 +432,31 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
             s = Mfma<T>::mma(rd_rows<D, PAD>(sK[buf], ks, lane), qf[ks], s);
             dp = Mfma<T>::mma(rd_rows<D, PAD>(sV[buf], ks, lane), dof[ks], dp);
         }
-        // key tiles before the diagonal and away from the ends need no mask (uniform)
-        const bool inner = qw0 + 32 <= Nq && 32 * t + 32 <= Nk && (!p.causal || 32 * t + 31 <= qw0);
+        // dS packed to 16 bit. Key tiles before the diagonal and away from the ends need no
+        // mask: a uniform branch picks the mask-free form; on edge tiles every exponential is
+        // taken and masked pairs are selected to 0 (no per-element branch).
         u32x4 dsf[2];
+        auto ds_of = [&](auto masked) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            float dsv[8];
+            for (int kk = 0; kk < 2; ++kk) {
+                float dsv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int kj = 32 * t + 16 * kk + 8 * h + e;
-                const bool vis = inner || (qi < Nq && kj < Nk && (!p.causal || kj <= qi));
-                const float pe = vis ? __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -lse2)) : 0.f;
-                dsv[e] = pe * (dp[8 * kk + e] - delta);
+                for (int e = 0; e < 8; ++e) {
+                    float pe = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -lse2));
+                    if constexpr (decltype(masked)::value) {
+                        const int kj = 32 * t + 16 * kk + 8 * h + e;
+                        const bool vis = qi < Nq && kj < Nk && (!p.causal || kj <= qi);
+                        pe = vis ? pe : 0.f;
+                    }
+                    dsv[e] = pe * (dp[8 * kk + e] - delta);
+                }
+                dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
+                                Mfma<T>::pack2(dsv[4], dsv[5]), Mfma<T>::pack2(dsv[6], dsv[7])};
             }
-            dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
-                            Mfma<T>::pack2(dsv[4], dsv[5]), Mfma<T>::pack2(dsv[6], dsv[7])};
-        }
+        };
+        const bool inner = qw0 + 32 <= Nq && 32 * t + 32 <= Nk && (!p.causal || 32 * t + 31 <= qw0);
+        if (inner) ds_of(std::false_type{});
+        else ds_of(std::true_type{});
         // dQ^T += K^T dS^T
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)

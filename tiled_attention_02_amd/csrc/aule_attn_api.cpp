@@ -369,6 +369,12 @@ aule_status_t aule_attn_bwd(const void* q, const void* k, const void* v, const v
             if (overlaps(outs[a], nout[a], outs[b2], nout[b2]))
                 return fail(AULE_ERR_INVALID_ARGUMENT, "gradient buffers overlap");
     }
+    // the matrix-core kernels address one (batch, head) slice with 32-bit buffer offsets
+    const aule::Dtype dt16 = static_cast<aule::Dtype>(dtype);
+    if ((dt16 == aule::Dtype::F16 || dt16 == aule::Dtype::BF16) &&
+        (size_t)(seqlen_q > seqlen_k ? seqlen_q : seqlen_k) * head_dim * es >= ((size_t)1 << 30))
+        return fail(AULE_ERR_UNSUPPORTED, "fp16/bf16 slice too large for 32-bit offsets: one (batch, head) slice "
+                    "must span less than 1 GiB");
     aule::BwdProblem p{};
     p.q = q; p.k = k; p.v = v; p.o = o; p.do_ = dout; p.lse = lse;
     p.dq = dq; p.dk = dk; p.dv = dv;
