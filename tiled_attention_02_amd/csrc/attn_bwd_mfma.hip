@@ -304,12 +304,13 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
                 float pv[8], dsv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    float pe = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -lq[e]));
+                    float x = fmaf(s[8 * kk + e], c2, -lq[e]);
                     if constexpr (decltype(masked)::value) {
                         const int qi = i0 + q0 + e;
                         const bool vis = qi < Nq && key < Nk && (!p.causal || key <= qi);
-                        pe = vis ? pe : 0.f;
+                        x = vis ? x : -INFINITY;   // exp2(-inf) = +0
                     }
+                    const float pe = __builtin_amdgcn_exp2f(x);
                     pv[e] = pe;
                     dsv[e] = PASS == 1 ? pe * dp[8 * kk + e] : 0.f;
                 }
@@ -442,12 +443,13 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
                 float dsv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    float pe = __builtin_amdgcn_exp2f(fmaf(s[8 * kk + e], c2, -lse2));
+                    float x = fmaf(s[8 * kk + e], c2, -lse2);
                     if constexpr (decltype(masked)::value) {
                         const int kj = 32 * t + 16 * kk + 8 * h + e;
                         const bool vis = qi < Nq && kj < Nk && (!p.causal || kj <= qi);
-                        pe = vis ? pe : 0.f;
+                        x = vis ? x : -INFINITY;   // exp2(-inf) = +0
                     }
+                    const float pe = __builtin_amdgcn_exp2f(x);
                     dsv[e] = pe * (dp[8 * kk + e] - delta);
                 }
                 dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),

@@ -46,6 +46,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
 
 #include "attn_device.h"
 #include "attn_mfma.h"
@@ -400,30 +401,50 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                               (p.win_left >= 0 && k0 < qhi - p.win_left) ||
                               (!CAUSAL && p.win_right >= 0 && k0 + 31 > qlo + p.win_right);
             const float slope_l2 = cur.slope * 1.4426950408889634f;
+            // The three conditions are uniform: each combination is a loop of its own (tested
+            // inside the unrolled loop they cost scalar compares and branches per score).
+            auto rewrite = [&](auto has_cap, auto has_slope, auto is_edge) {
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) {
-                const int qi = qlo + 32 * nb + ln;
-                const float fb = (float)(qi - k0 - 8 * h);   // qi - key = fb - (key offset)
+                for (int nb = 0; nb < NB; ++nb) {
+                    const int qi = qlo + 32 * nb + ln;
+                    const float fb = (float)(qi - k0 - 8 * h);   // qi - key = fb - (key offset)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int koff_r = 16 * (r >> 3) + (r & 7);
-                    float x;
-                    if (cap > 0.f) {
-                        const float e = __builtin_amdgcn_exp2f(acc[nb][r] * cap_k);
-                        x = fmaf(-2.f * cap_l2, __builtin_amdgcn_rcpf(e + 1.f), cap_l2);
-                    } else {
-                        x = acc[nb][r] * c;
+                    for (int r = 0; r < 16; ++r) {
+                        const int koff_r = 16 * (r >> 3) + (r & 7);
+                        float x;
+                        if constexpr (decltype(has_cap)::value) {
+                            const float e = __builtin_amdgcn_exp2f(acc[nb][r] * cap_k);
+                            x = fmaf(-2.f * cap_l2, __builtin_amdgcn_rcpf(e + 1.f), cap_l2);
+                        } else {
+                            x = acc[nb][r] * c;
+                        }
+                        if constexpr (decltype(has_slope)::value) x = fmaf(-slope_l2, fabsf(fb - (float)koff_r), x);
+                        if constexpr (decltype(is_edge)::value) {
+                            // keep the rewrite unconditional: left alone, the compiler moves it
+                            // under a per-score branch on the mask
+                            asm volatile("" : "+v"(x));
+                            const int key = k0 + 8 * h + koff_r;
+                            const bool masked = (key >= cur.Lk) || (CAUSAL && key > qi) ||
+                                                (p.win_left >= 0 && key < qi - p.win_left) ||
+                                                (!CAUSAL && p.win_right >= 0 && key > qi + p.win_right);
+                            x = masked ? -INFINITY : x;
+                        }
+                        acc[nb][r] = x;
                     }
-                    if (slope_l2 != 0.f) x = fmaf(-slope_l2, fabsf(fb - (float)koff_r), x);
-                    if (edge) {
-                        const int key = k0 + 8 * h + koff_r;
-                        const bool masked = (key >= cur.Lk) || (CAUSAL && key > qi) ||
-                                            (p.win_left >= 0 && key < qi - p.win_left) ||
-                                            (!CAUSAL && p.win_right >= 0 && key > qi + p.win_right);
-                        x = masked ? -INFINITY : x;
-                    }
-                    acc[nb][r] = x;
                 }
+            };
+            using Y = std::true_type;
+            using N = std::false_type;
+            auto by_edge = [&](auto has_cap, auto has_slope) {
+                if (edge) rewrite(has_cap, has_slope, Y{});
+                else rewrite(has_cap, has_slope, N{});
+            };
+            if (cap > 0.f) {
+                if (slope_l2 != 0.f) by_edge(Y{}, Y{});
+                else by_edge(Y{}, N{});
+            } else {
+                if (slope_l2 != 0.f) by_edge(N{}, Y{});
+                else by_edge(N{}, N{});
             }
             return;
         }
