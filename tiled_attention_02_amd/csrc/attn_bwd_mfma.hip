@@ -193,9 +193,13 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     const int j0 = kb * 32 * WV;
     const int key = j0 + 32 * wave + ln;                 // this lane's key (B-operand column)
     const int64_t kv_off = ((int64_t)b * p.heads_kv + hk) * Nk * d;
-    // work: (query head g of the group, QR-row query tile), causal from the first key on.
-    // With no query rows (nit == 0) only the zero gradients are written: q, k, v, o, do and
-    // lse may then be null and are not read.
+    // work: (QR-row query tile, query head g of the group), causal from the first key on.
+    // The tiles are walked from the last one down, the group's heads inner, so that the
+    // workgroups of one (batch, kv head) — which run on one XCD, whatever their first key —
+    // read the same Q / dO / O tile at the same time and share it through that XCD's L2
+    // (walked upwards from each block's first key, they read different rows: -2.5% time on the
+    // bf16 causal GQA backward). With no query rows (nit == 0) only the zero gradients are
+    // written: q, k, v, o, do and lse may then be null and are not read.
     const int i_start = p.causal ? j0 : 0;
     const int ntile = Nq > i_start ? (Nq - i_start + QR - 1) / QR : 0;
     const int nit = G * ntile;
@@ -219,7 +223,7 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
         float lse;
     };
     auto fetch = [&](int it, Stage& st) {
-        const int g = it / ntile, i0 = i_start + QR * (it - g * ntile);
+        const int tr = it / G, g = it - tr * G, i0 = i_start + QR * (ntile - 1 - tr);
         const int64_t bh = (int64_t)b * p.heads_q + hk * G + g;
         const int64_t q_off = bh * Nq * d;
         const __amdgpu_buffer_rsrc_t rq = slice_rsrc(static_cast<const T*>(p.q) + q_off, Nq, d);
@@ -262,7 +266,7 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     const int kw0 = j0 + 32 * wave;   // this wave's first key
     auto body = [&](int it, Stage& mine, const Stage& other) {
         const int buf = it & 1;
-        const int g = it / ntile, i0q = i_start + QR * (it - g * ntile);
+        const int i0q = i_start + QR * (ntile - 1 - it / G);
         if (it + 2 < nit) fetch(it + 2, mine);
 #pragma unroll
         for (int hf = 0; hf < QH; ++hf) {

@@ -56,7 +56,7 @@ namespace {
 
 [[maybe_unused]] constexpr float kRescaleSlack = 8.0f; // log2 units
 [[maybe_unused]] constexpr float kSlackExp = 256.0f;   // 2^kRescaleSlack
-constexpr int kCopyParts = 4;                           // pieces of one K/V tile copy
+[[maybe_unused]] constexpr int kCopyParts = 4;          // pieces of one K/V tile copy
 
 #if defined(__HIP_DEVICE_COMPILE__)
 // Start the global -> LDS copy of one K/V tile: NI 16-byte loads per lane for each of K and
