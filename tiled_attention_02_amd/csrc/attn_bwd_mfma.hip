@@ -222,10 +222,18 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
         u32x4 q[QH][TL::NCH], dO[QH][TL::NCH], o[QH][PASS == 1 ? TL::NCH : 1];
         float lse;
     };
-    auto fetch = [&](int it, Stage& st) {
-        const int tr = it / G, g = it - tr * G, i0 = i_start + QR * (ntile - 1 - tr);
-        const int64_t bh = (int64_t)b * p.heads_q + hk * G + g;
+    // (tile counted from the last, head) of the next fetch and of the current body: advanced
+    // one step per iteration instead of dividing the iteration index by the group size
+    int f_tr = 0, f_g = 0, b_tr = 0, b_g = 0;
+    auto step = [&](int& tr, int& g) {
+        if (++g == G) { g = 0; ++tr; }
+    };
+    const int64_t bh0 = (int64_t)b * p.heads_q + (int64_t)hk * G;
+    auto fetch = [&](Stage& st) {
+        const int i0 = i_start + QR * (ntile - 1 - f_tr);
+        const int64_t bh = bh0 + f_g;
         const int64_t q_off = bh * Nq * d;
+        step(f_tr, f_g);
         const __amdgpu_buffer_rsrc_t rq = slice_rsrc(static_cast<const T*>(p.q) + q_off, Nq, d);
         const __amdgpu_buffer_rsrc_t rdo = slice_rsrc(static_cast<const T*>(p.do_) + q_off, Nq, d);
 #pragma unroll
@@ -266,8 +274,9 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     const int kw0 = j0 + 32 * wave;   // this wave's first key
     auto body = [&](int it, Stage& mine, const Stage& other) {
         const int buf = it & 1;
-        const int i0q = i_start + QR * (ntile - 1 - it / G);
-        if (it + 2 < nit) fetch(it + 2, mine);
+        const int i0q = i_start + QR * (ntile - 1 - b_tr);
+        step(b_tr, b_g);
+        if (it + 2 < nit) fetch(mine);
 #pragma unroll
         for (int hf = 0; hf < QH; ++hf) {
         const int i0 = i0q + 32 * hf;
@@ -344,10 +353,10 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
 
     Stage st0, st1;
     if (nit > 0) {
-        fetch(0, st0);
+        fetch(st0);
         commit(0, st0);
     }
-    if (nit > 1) fetch(1, st1);
+    if (nit > 1) fetch(st1);
     __syncthreads();
     for (int it = 0; it < nit; it += 2) {
         body(it, st0, st1);
