@@ -159,9 +159,12 @@ aule_status_t aule_attn_fwd_varlen_mods(const void* qkv, const int32_t* cu_seqle
  *
  *   q, o : [batch, heads_q, seqlen_q, head_dim] contiguous, dtype
  *   k, v : [batch, heads_kv, seqlen_k, head_dim] contiguous, dtype
- *   num_splits : key-range splits; 0 chooses about 1024 / (batch * heads_kv) (at least 1);
- *                any value is clamped to [1, ceil(seqlen_k / tile)] with tile = 64 keys
- *                (32 for fp32), and splits that would be empty are dropped
+ *   num_splits : key-range splits; 0 chooses about C / (batch * heads_kv) (at least 1), with
+ *                C the device's compute-unit count for fp16/bf16 problems of at most 32
+ *                query rows per kv head (head_dim <= 128: the matrix-core kernel, one
+ *                workgroup per CU) and C = 1024 otherwise; any value is clamped to
+ *                [1, ceil(seqlen_k / tile)] with tile = 128 keys for those matrix-core
+ *                problems, else 64 (32 for fp32), and splits that would be empty are dropped
  *
  * batch == 0 or seqlen_q == 0 is an empty problem (AULE_OK, nothing launched). Besides the
  * rules of aule_attn_fwd: (heads_q / heads_kv) * seqlen_q <= 64 query rows per kv head

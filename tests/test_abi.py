@@ -208,8 +208,12 @@ def test_splitkv_workspace_size(lib):
     # more splits than tiles are clamped; fp32 tiles are 32 keys
     assert ws(1, 1, 1, 1, 64, 64, F16, 100) == 256 + 1 * 1 * 64 * 4
     assert ws(1, 1, 1, 1, 64, 64, F32, 100) == 256 + 2 * 1 * 64 * 4
-    # automatic choice: about 1024 / (batch * heads_kv) splits, clamped to the tiles
-    assert ws(2, 8, 2, 1, 1 << 16, 64, BF16, 0) == ws(2, 8, 2, 1, 1 << 16, 64, BF16, 256)
+    # automatic choice: about C / (batch * heads_kv) splits, clamped to the tiles; C = 1024
+    # for the vector-ALU kernel, the CU count (256 on MI355X, and without a device) for the
+    # matrix-core one (16-bit, at most 32 query rows per kv head)
+    assert ws(2, 8, 2, 1, 1 << 16, 64, F32, 0) == ws(2, 8, 2, 1, 1 << 16, 64, F32, 256)
+    assert ws(2, 8, 2, 1, 1 << 16, 64, BF16, 0) == ws(2, 8, 2, 1, 1 << 16, 64, BF16, 64)
+    assert ws(2, 8, 2, 16, 1 << 16, 64, BF16, 0) == ws(2, 8, 2, 16, 1 << 16, 64, BF16, 256)
     # empty or rejected arguments -> 0
     assert ws(0, 8, 2, 1, 100, 64, BF16, 0) == 0
     assert ws(1, 8, 3, 1, 100, 64, BF16, 0) == 0 and aule.aule_last_error() != ""

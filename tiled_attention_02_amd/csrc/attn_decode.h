@@ -37,6 +37,14 @@ struct DecodeProblem {
 int decode_keys_per_tile(Dtype dt);
 // Launches the partial kernel and the merge kernel on `stream`; does not synchronise.
 hipError_t launch_attn_decode(const DecodeProblem& p, Dtype dt, hipStream_t stream);
+// The matrix-core partial kernel (fp16/bf16, at most 32 query rows per kv head, head_dim up
+// to 128): whether it covers a problem, and its launch (same workspace layout).
+bool decode_mfma_supports(const DecodeProblem& p, Dtype dt);
+// Whether a problem shape takes the matrix-core kernel (decided before the split plan), and
+// the key granule its splits should be a multiple of (every wave gets whole tiles).
+bool decode_mfma_eligible(Dtype dt, int rows_per_kv_head, int head_dim);
+int decode_mfma_keys_granule();
+hipError_t launch_attn_decode_mfma_partial(const DecodeProblem& p, Dtype dt, hipStream_t stream);
 // The fixed device workspace of the no-allocation entry point: its size, and its address on
 // the current device (looked up once per device).
 size_t decode_scratch_bytes();

@@ -32,6 +32,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "attn_decode.h"
 
@@ -440,7 +441,10 @@ hipError_t launch_partial(const DecodeProblem& p, hipStream_t stream) {
 
 template <typename T>
 hipError_t launch_t(const DecodeProblem& p, hipStream_t stream) {
-    hipError_t e = p.head_dim <= 64 ? launch_partial<T, 64>(p, stream) : launch_partial<T, 128>(p, stream);
+    const Dtype dt = std::is_same<T, float>::value ? Dtype::F32 : std::is_same<T, bf16_t>::value ? Dtype::BF16 : Dtype::F16;
+    hipError_t e = decode_mfma_supports(p, dt) ? launch_attn_decode_mfma_partial(p, dt, stream)
+                   : p.head_dim <= 64          ? launch_partial<T, 64>(p, stream)
+                                               : launch_partial<T, 128>(p, stream);
     if (e != hipSuccess) return e;
     const int64_t rows = (int64_t)p.batch * p.heads_q * p.seqlen_q;
     hipLaunchKernelGGL((attn_decode_combine_kernel<T>), dim3((unsigned)rows), dim3(64), 0, stream, p);

@@ -85,7 +85,19 @@ struct SplitPlan {
     size_t bytes;      // total workspace
 };
 
-constexpr int64_t kSplitTargetWorkgroups = 1024;   // about four per CU on a 256-CU device
+constexpr int64_t kSplitTargetWorkgroups = 1024;   // vector-ALU kernel: about four per CU on 256 CUs
+
+// The matrix-core partial kernel holds one workgroup per CU (128 KiB of LDS at head_dim
+// 128): one workgroup per CU, so that every split runs in the first and only round.
+int64_t resident_cus() {
+    static const int64_t n = [] {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess) return 256;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+        return cus;
+    }();
+    return n;
+}
 
 aule_status_t check_splitkv(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_q,
                             int32_t seqlen_k, int32_t head_dim, int32_t causal, aule_dtype_t dtype,
@@ -109,6 +121,9 @@ aule_status_t check_splitkv(int32_t batch, int32_t heads_q, int32_t heads_kv, in
                     (heads_q / heads_kv) * seqlen_q);
     if ((int64_t)batch * heads_q * seqlen_q > INT32_MAX)
         return fail(AULE_ERR_INVALID_ARGUMENT, "too many output rows");
+    if (dtype != AULE_DTYPE_F32 && (int64_t)seqlen_k * head_dim * 2 >= ((int64_t)1 << 30))
+        return fail(AULE_ERR_UNSUPPORTED, "fp16/bf16 slice too large for 32-bit offsets: one (batch, kv head) "
+                    "cache slice must span less than 1 GiB");
     if (batch > 65535 || heads_kv > 65535)   // grid z and y dimensions
         return fail(AULE_ERR_UNSUPPORTED, "batch and heads_kv must be at most 65535 for split-KV decoding");
     return AULE_OK;
@@ -116,10 +131,13 @@ aule_status_t check_splitkv(int32_t batch, int32_t heads_q, int32_t heads_kv, in
 
 SplitPlan plan_splits(int32_t batch, int32_t heads_q, int32_t heads_kv, int32_t seqlen_q,
                       int32_t seqlen_k, int32_t head_dim, aule_dtype_t dtype, int32_t num_splits) {
-    const int64_t tk = aule::decode_keys_per_tile(static_cast<aule::Dtype>(dtype));
+    const aule::Dtype dt = static_cast<aule::Dtype>(dtype);
+    const bool mfma = heads_kv > 0 && aule::decode_mfma_eligible(dt, heads_q / heads_kv * seqlen_q, head_dim);
+    const int64_t tk = mfma ? aule::decode_mfma_keys_granule() : aule::decode_keys_per_tile(dt);
     const int64_t tiles = (seqlen_k + tk - 1) / tk;
     const int64_t groups = (int64_t)batch * heads_kv;
-    int64_t s = num_splits > 0 ? num_splits : (kSplitTargetWorkgroups + groups - 1) / groups;
+    const int64_t target = mfma ? resident_cus() : kSplitTargetWorkgroups;
+    int64_t s = num_splits > 0 ? num_splits : (target + groups - 1) / groups;
     s = s < 1 ? 1 : (s > tiles ? tiles : s);
     const int64_t kps = (tiles + s - 1) / s * tk;           // whole tiles per split
     s = (seqlen_k + kps - 1) / kps;                         // no empty split
