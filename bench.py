@@ -35,7 +35,9 @@ KERNEL_SOURCES = ["tiled_attention_02_amd/csrc/attn_fwd_mfma.hip",
                   "tiled_attention_02_amd/csrc/attn_problem.h",
                   "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
 DECODE_SOURCES = ["tiled_attention_02_amd/csrc/attn_decode.hip",
+                  "tiled_attention_02_amd/csrc/attn_decode_mfma.hip",
                   "tiled_attention_02_amd/csrc/attn_decode.h",
+                  "tiled_attention_02_amd/csrc/attn_mfma.h",
                   "tiled_attention_02_amd/csrc/attn_device.h",
                   "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
 BWD_SOURCES = ["tiled_attention_02_amd/csrc/attn_bwd_mfma.hip",
