@@ -82,8 +82,8 @@ __global__ __launch_bounds__(kWaves * 64) void attn_decode_mfma_kernel(DecodePro
         const uint32_t kdst = lds_of(sbuf[wave][stg][0]), vdst = lds_of(sbuf[wave][stg][1]);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            lds_copy16(rk, koff[i] + key0 * row_bytes, __builtin_amdgcn_readfirstlane(kdst + (uint32_t)i * 1024u));
-            lds_copy16(rv, voff[i] + key0 * row_bytes, __builtin_amdgcn_readfirstlane(vdst + (uint32_t)i * 1024u));
+            lds_copy16_stream(rk, koff[i] + key0 * row_bytes, __builtin_amdgcn_readfirstlane(kdst + (uint32_t)i * 1024u));
+            lds_copy16_stream(rv, voff[i] + key0 * row_bytes, __builtin_amdgcn_readfirstlane(vdst + (uint32_t)i * 1024u));
         }
     };
     if (nmine > 0) issue(0);

@@ -119,6 +119,23 @@ __device__ __forceinline__ void lds_copy16(i32x4 rsrc, uint32_t voffset, uint32_
         : "v"(voffset), "s"(rsrc), "s"(lds_addr));
 }
 
+// The same copy marked non-temporal (nt): for data read exactly once, such as a decode's
+// K/V cache. The line is not kept in the caches for reuse, which lifts a pure stream from
+// about 6.0 to about 7.0 TB/s on gfx950; data that other workgroups read again (the tiled
+// forward's K/V) keeps the default policy.
+__device__ __forceinline__ void lds_copy16_stream(i32x4 rsrc, uint32_t voffset, uint32_t lds_addr) {
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen nt lds\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(voffset), "s"(rsrc), "s"(lds_addr));
+}
+
 // Raw buffer descriptor (stride 0, bounds-checked by num_records bytes).
 __device__ __forceinline__ i32x4 buffer_desc(const void* base, int num_records) {
     const uint64_t b = reinterpret_cast<uint64_t>(base);
