@@ -58,6 +58,25 @@ void attn_fwd_short_kernel(AttnProblem p, int n_rb) {
     const uint32_t q_rs = (uint32_t)(p.q_rstride * (int64_t)sizeof(T));
     const uint32_t o_rs = (uint32_t)(p.o_rstride * (int64_t)sizeof(T));
 
+    // Q^T of an item as B operands: lane column = query qr0 + ln; rows past Lq and columns
+    // past head_dim read as zero through the descriptor bound and the out-of-range offset
+    const int n_items = p.group * n_rb;
+    u32x4 qf[KS];
+    auto load_q = [&](int it) {
+        const int g = it / n_rb, rb = it - g * n_rb;
+        const T* qb = static_cast<const T*>(p.q) + b * p.q_bstride + (hk * p.group + g) * p.q_hstride;
+        const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T*>(qb), (short)0, (int)((int64_t)Lq * q_rs), (int)kBufferFlags);
+        const uint32_t off = (uint32_t)(32 * rb + ln) * q_rs + (uint32_t)h * 16u;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint32_t o = (2 * ks + h) * 8 < hd ? off + (uint32_t)ks * 32u : kOobOffset;
+            qf[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)o, 0, 0));
+        }
+    };
+    // the first item's Q is fetched together with K and V, so that the two fetches overlap
+    if (wave < n_items) load_q(wave);
+
     // ------------------------------------------------ K, V of the slice -> LDS (zero-padded)
     {
         const T* kb = static_cast<const T*>(p.k) + b * p.k_bstride + hk * p.k_hstride;
@@ -95,28 +114,17 @@ void attn_fwd_short_kernel(AttnProblem p, int n_rb) {
 
     const bool neg = p.scale_log2 < 0.f;
     const float c = fmaxf(fabsf(p.scale_log2), 1e-30f);
-    const int n_items = p.group * n_rb;
 
     for (int it = wave; it < n_items; it += WAVES) {
         const int g = it / n_rb, rb = it - g * n_rb;
         const int hq = hk * p.group + g;
         const int qr0 = 32 * rb;
-        const T* qb = static_cast<const T*>(p.q) + b * p.q_bstride + hq * p.q_hstride;
         T* ob = static_cast<T*>(p.o) + b * p.o_bstride + hq * p.o_hstride;
 
-        // Q^T as B operands: lane column = query qr0 + ln (rows past Lq read as zero)
-        u32x4 qf[KS];
-        {
-            const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<T*>(qb), (short)0, (int)((int64_t)Lq * q_rs), (int)kBufferFlags);
-            const uint32_t off = (uint32_t)(qr0 + ln) * q_rs + (uint32_t)h * 16u;
+        if (it != wave) load_q(it);
+        if (neg)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                qf[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rq, (int)off, ks * 32, 0));
-                if ((2 * ks + h) * 8 >= hd) qf[ks] = u32x4{0u, 0u, 0u, 0u};
-                if (neg) qf[ks] ^= 0x80008000u;   // a negative scale flips the sign of Q exactly
-            }
-        }
+            for (int ks = 0; ks < KS; ++ks) qf[ks] ^= 0x80008000u;   // a negative scale flips the sign of Q exactly
 
         // full score rows: block j holds keys 32j + 16(r/8) + 8h + r%8 of query qr0 + ln
         const int kend = CAUSAL ? min(Lk, qr0 + 32) : Lk;
