@@ -140,7 +140,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     constexpr int NBUF = 2;                      // LDS tile buffers (double buffering)
     constexpr int AHEAD = 1;                     // tiles requested ahead
     constexpr int DMA_PARTS = kCopyParts < SPT ? kCopyParts : SPT;   // pieces of a tile copy
-    constexpr int NSTORE = NB * DB * 4;          // O store instructions per wave and work item
+    constexpr int NSTORE = NB * (DB / 2) * 4;    // O store instructions per wave and item (slab path)
     static_assert(TB == 64 || TB == 128, "tile of 64 or 128 keys");
     static_assert(!PERSIST || !VARLEN, "persistent form: dense problems");
     constexpr int TILE_CHUNKS = kBN * KC;        // 16-byte chunks per K (or V) tile
@@ -149,6 +149,10 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
 
     __shared__ u32x4 sK[NBUF][TILE_CHUNKS];
     __shared__ u32x4 sV[NBUF][TILE_CHUNKS];
+    // persistent form: a private 4 KiB slab per wave (32 rows x 128 bytes) through which O
+    // is written out in whole row segments (the LDS left over next to the K/V buffers)
+    constexpr int kSlab = PERSIST ? 256 : 1;
+    __shared__ u32x4 sO[PERSIST ? WAVES : 1][kSlab];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -584,7 +588,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     // O = O^T accumulators / l, rounded to T, through buffer stores whose descriptor covers
     // exactly the Lq valid rows of this wave's slice: rows past the end and columns past
     // head_dim (given an offset past the descriptor) are dropped by the hardware, so every
-    // wave issues exactly NSTORE store instructions per item, with no branch.
+    // wave issues the same store instructions per item, with no branch (non-persistent forms).
     auto store_o = [&]() {
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
             cur.ob, (short)0, cur.Lq > 0 ? (int)((int64_t)cur.Lq * o_rs) : 0, (int)kBufferFlags);
@@ -610,6 +614,58 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
         }
         // after the O stores: the persistent form's wait for the next item only needs every
         // store to be newer than that item's loads
+        if (cur.lseb) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = cur.qr0 + 32 * nb + ln;
+                if (h == 0 && row < cur.Lq) cur.lseb[row] = lse_row[nb];
+            }
+        }
+    };
+
+    // Persistent form: the same O, staged through the wave's LDS slab so that each store
+    // instruction writes 8 whole 128-byte row segments (the accumulator layout above gives
+    // every store 32 rows x 16 bytes: 32 cache lines per instruction, which left the memory
+    // pipeline of every CU busy for thousands of cycles when all workgroups finished an item
+    // at once, with the next item's loads and tile copies queued behind the stores). One
+    // 64-column half of the rows at a time: 8 stores of 8 bytes per lane into the slab (16-byte
+    // chunk c of row r sits at c ^ ((r / 2) % 8): every write pass hits distinct banks), then
+    // 4 reads of 8 rows x 128 contiguous bytes, each lane storing its chunk where it belongs.
+    // The slab is this wave's alone and LDS operations of one wave complete in order, so no
+    // wait or barrier is needed between the writes, the reads and the next half's writes.
+    auto store_o_slab = [&]() {
+        const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+            cur.ob, (short)0, cur.Lq > 0 ? (int)((int64_t)cur.Lq * o_rs) : 0, (int)kBufferFlags);
+        char* slab = reinterpret_cast<char*>(sO[PERSIST ? wave : 0]);
+        float lse_row[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const float l = l_part[nb] + __shfl_xor(l_part[nb], 32);
+            const float inv = 1.f / l;
+            lse_row[nb] = (m_ref[nb] + __builtin_amdgcn_logf(l)) * 0.69314718055994531f;
+#pragma unroll
+            for (int hr = 0; hr < DB / 2; ++hr) {
+#pragma unroll
+                for (int dbl = 0; dbl < 2; ++dbl)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x16& a = o[2 * hr + dbl][nb];
+                        const u32x2 w = {Mfma<T>::pack2(a[4 * g] * inv, a[4 * g + 1] * inv),
+                                         Mfma<T>::pack2(a[4 * g + 2] * inv, a[4 * g + 3] * inv)};
+                        const int cs = (4 * dbl + g) ^ ((ln >> 1) & 7);
+                        *reinterpret_cast<u32x2*>(slab + ln * 128 + cs * 16 + h * 8) = w;
+                    }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int row = 8 * k + (lane >> 3), slot = lane & 7;
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(slab + row * 128 + slot * 16);
+                    const int d0 = 64 * hr + 8 * (slot ^ ((row >> 1) & 7));
+                    const uint32_t off = d0 < hd ? (uint32_t)(cur.qr0 + 32 * nb + row) * o_rs + (uint32_t)d0 * (uint32_t)sizeof(T)
+                                                 : kOobOffset;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)off, 0, 0);
+                }
+            }
+        }
         if (cur.lseb) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
@@ -650,8 +706,9 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                 if (t >= cur.n_kt) break;
                 const int b = (u + P) % NBUF;
                 const int bn = (u + P + AHEAD) % NBUF;          // buffer of tile t + AHEAD
-                // at tile 0 of a later item the previous item's NSTORE stores are the newest
-                // memory operations and may stay in flight
+                // at tile 0 of a later item the previous item's NSTORE O stores (and its LSE
+                // stores after them) are the newest memory operations: vmcnt(NSTORE) still
+                // waits for the copy and the Q loads issued before them
                 if (PERSIST && t == 0 && !first) wait_vmcnt_barrier<NSTORE>();
                 else wait_vmcnt_barrier<0>();
                 // Fragment reads run one step ahead of their use: after the S^T products of
@@ -713,7 +770,7 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
             if (par == 0) run_item(Parity<0>{}, r == 0, more, nxt);
             else run_item(Parity<1>{}, r == 0, more, nxt);
             if (more) load_q(nxt);   // Q is dead after this item's last S^T products
-            store_o();
+            store_o_slab();
             if (!more) break;
             par = (par + cur.n_kt) & 1;
             cur = nxt;
