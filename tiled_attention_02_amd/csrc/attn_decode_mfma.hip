@@ -8,8 +8,8 @@
 // never written). A workgroup of 4 waves takes one (split, kv head, batch); wave w walks
 // the split's 32-key tiles w, w + 4, ... on its own: each wave has a private two-stage LDS
 // ring filled by buffer_load ... lds copies (the K and V tile swizzles of the forward
-// kernel), so the loop has no barrier, and one copy is in flight while the other tile is
-// consumed. At the end the four waves' (m, l, O) are merged through LDS and written to the
+// kernel; marked non-temporal, since every cache byte is read once), so the loop has no
+// barrier, and one copy is in flight while the other tile is consumed. At the end the four waves' (m, l, O) are merged through LDS and written to the
 // workspace in the layout the merge kernel of attn_decode.hip reads.
 #include <hip/hip_runtime.h>
 #include <math.h>
