@@ -94,6 +94,16 @@ def measured_traffic(workload):
     return None
 
 
+def traffic_source(workload):
+    """Where `traffic` comes from: it is not measured in this run but read from the committed
+    counter record, and only when that record was taken on the current kernel sources."""
+    sha = kernel_source_hash(sources_for(workload))
+    if measured_traffic(workload) is None:
+        return f"no rocprofv3 record in profiles/traffic.json for kernel sources {sha}"
+    return (f"rocprofv3 FETCH_SIZE + WRITE_SIZE record in profiles/traffic.json, taken on kernel "
+            f"sources {sha} (the current ones), scaled by a 256 MiB copy calibration")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -415,6 +425,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(cfg.name),
+                     "traffic_source": traffic_source(cfg.name),
                      "kernel_ms": round(kern_s * 1e3, 4),
                      "launch_ms": {"median": round(launches[len(launches) // 2] * 1e3, 4),
                                    "min": round(launches[0] * 1e3, 4),
