@@ -248,6 +248,15 @@ def test_batch_and_longer_dense():
     check_dense(2, 4, 1, 700, 900, 128, "bf16", False, seed=23)
 
 
+def test_persistent_items_ragged_padded_head_dim():
+    """More work items than resident workgroups, so each persistent workgroup walks several:
+    the item switch (next item's Q loads, O written through the per-wave LDS slab, the next
+    tile copy in flight) runs with a ragged last q-tile (rows past the end dropped) and a
+    head_dim below the kernel's 128 (columns past it dropped): 512 and 480 items."""
+    check_dense(4, 32, 8, 1000, 1000, 96, "bf16", True, seed=31)
+    check_dense(8, 16, 4, 900, 900, 72, "f16", False, seed=32)
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_xcd_group_major_dense(causal):
     """(batch, query-head group) counts that divide by 8 take the XCD-local, group-major item
