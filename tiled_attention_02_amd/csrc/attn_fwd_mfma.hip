@@ -629,14 +629,16 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
     // pipeline of every CU busy for thousands of cycles when all workgroups finished an item
     // at once, with the next item's loads and tile copies queued behind the stores). One
     // 64-column half of the rows at a time: 8 stores of 8 bytes per lane into the slab (16-byte
-    // chunk c of row r sits at c ^ ((r / 2) % 8): every write pass hits distinct banks), then
-    // 4 reads of 8 rows x 128 contiguous bytes, each lane storing its chunk where it belongs.
+    // chunk c of row r sits at c ^ ((r / 2) % 8), its two 8-byte halves swapped in rows 16-31,
+    // so that the 32 lanes of each write pass cover all 64 banks once), then 4 reads of 8 rows
+    // x 128 contiguous bytes, each lane storing its chunk where it belongs (the reads of rows
+    // 16-31 swap the halves back: a renaming of registers).
     // The slab is this wave's alone and LDS operations of one wave complete in order, so no
     // wait or barrier is needed between the writes, the reads and the next half's writes.
     auto store_o_slab = [&]() {
         const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
             cur.ob, (short)0, cur.Lq > 0 ? (int)((int64_t)cur.Lq * o_rs) : 0, (int)kBufferFlags);
-        char* slab = reinterpret_cast<char*>(sO[PERSIST ? wave : 0]);
+        char* slab = reinterpret_cast<char*>(sO[PERSIST ? wave : 0]);   // called in the persistent form only
         float lse_row[NB];
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
@@ -653,12 +655,13 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                         const u32x2 w = {Mfma<T>::pack2(a[4 * g] * inv, a[4 * g + 1] * inv),
                                          Mfma<T>::pack2(a[4 * g + 2] * inv, a[4 * g + 3] * inv)};
                         const int cs = (4 * dbl + g) ^ ((ln >> 1) & 7);
-                        *reinterpret_cast<u32x2*>(slab + ln * 128 + cs * 16 + h * 8) = w;
+                        *reinterpret_cast<u32x2*>(slab + ln * 128 + cs * 16 + (h ^ (ln >> 4)) * 8) = w;
                     }
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const int row = 8 * k + (lane >> 3), slot = lane & 7;
-                    const u32x4 v = *reinterpret_cast<const u32x4*>(slab + row * 128 + slot * 16);
+                    u32x4 v = *reinterpret_cast<const u32x4*>(slab + row * 128 + slot * 16);
+                    if (k >= 2) v = u32x4{v[2], v[3], v[0], v[1]};   // rows 16-31: halves swapped
                     const int d0 = 64 * hr + 8 * (slot ^ ((row >> 1) & 7));
                     const uint32_t off = d0 < hd ? (uint32_t)(cur.qr0 + 32 * nb + row) * o_rs + (uint32_t)d0 * (uint32_t)sizeof(T)
                                                  : kOobOffset;
