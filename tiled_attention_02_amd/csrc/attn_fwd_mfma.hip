@@ -665,7 +665,10 @@ void attn_fwd_mfma_kernel(AttnProblem p, int n_qtiles) {
                     const int d0 = 64 * hr + 8 * (slot ^ ((row >> 1) & 7));
                     const uint32_t off = d0 < hd ? (uint32_t)(cur.qr0 + 32 * nb + row) * o_rs + (uint32_t)d0 * (uint32_t)sizeof(T)
                                                  : kOobOffset;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)off, 0, 0);
+                    // non-temporal: each instruction writes 8 whole lines that no one here
+                    // reads again (-1.5 to -3% per launch on the bf16 causal GQA workload; the
+                    // same policy on Q loads, read once too, was slower)
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)off, 0, 2);
                 }
             }
         }
