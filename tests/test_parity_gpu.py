@@ -242,6 +242,27 @@ def test_scales(dtype, which):
         check_dense(1, 2, 1, 150, 150, d, dtype, causal, scale=scale, seed=11)
 
 
+def test_f32_matrix_core_shapes():
+    """fp32 problems on the fp32 matrix-core kernel: scale 1 at head_dim 128 (11x the default
+    scale; each score's 64 product steps in four chains), GQA groups of 4 and 2 over many
+    32-key tiles with a ragged last tile, cross lengths at a padded head_dim, and a varlen pack
+    at head_dim 128. (Scale 2 is swept at head_dim 64 above; at head_dim 128 the scores reach
+    ~115 in log2 units and rounding them once to fp32 already costs 8.2e-6 against the exact
+    result, computed with these inputs, so that case would test fp32 rather than the kernel.)"""
+    for causal in (False, True):
+        check_dense(1, 2, 1, 150, 150, 128, "f32", causal, scale=1.0, seed=12)
+    check_dense(2, 8, 2, 333, 333, 128, "f32", True, seed=13)
+    check_dense(1, 8, 4, 200, 517, 96, "f32", False, seed=14)
+    lengths = [300, 1, 129, 0, 64, 700]
+    for causal in (False, True):
+        say(f"varlen f32 lengths={lengths} causal={causal}")
+        qkv, cu = varlen_inputs(lengths, 4, 128, seed=15, dtype="f32")
+        got = run_varlen(qkv, cu, "f32", causal, 1 / math.sqrt(128))
+        ref = oracle.attention_ref_varlen(qkv, cu, causal=causal, scale=1 / math.sqrt(128))
+        assert np.all(np.isfinite(got))
+        assert np.max(np.abs(got - ref)) <= TOL["f32"]
+
+
 def test_batch_and_longer_dense():
     check_dense(3, 8, 2, 1000, 1000, 128, "bf16", True, seed=21)
     check_dense(2, 4, 4, 1500, 1500, 64, "f16", True, seed=22)

@@ -52,6 +52,10 @@ struct AttnProblem {
 
 // Launchers. Each returns hipSuccess or the launch error; none synchronises.
 hipError_t launch_attn_fwd_valu(const AttnProblem& p, Dtype dt, hipStream_t stream);
+// fp32 on the matrix cores (full-precision fp32 products); score modifiers and slices past
+// the kernel's 32-bit offsets stay on the vector-ALU kernel
+hipError_t launch_attn_fwd_f32_mfma(const AttnProblem& p, Dtype dt, hipStream_t stream);
+bool f32_mfma_supports(const AttnProblem& p, Dtype dt);
 hipError_t launch_attn_fwd_mfma(const AttnProblem& p, Dtype dt, hipStream_t stream);
 // True when the MFMA path handles this problem (fp16/bf16 and a supported head_dim).
 bool mfma_supports(const AttnProblem& p, Dtype dt);

@@ -54,14 +54,17 @@ hipError_t launch_bwd(const aule::BwdProblem& p, aule_dtype_t dtype, hipStream_t
     return aule::launch_attn_bwd(p, dt, stream);
 }
 
-// fp32 runs on the vector-ALU kernel; fp16/bf16 on the matrix cores: the short-sequence
-// kernel for at most 128 keys, else the tiled kernel. A 16-bit problem that neither covers
-// (a (sequence, head) slice of 1 GiB or more) is refused, never sent to another kernel.
+// fp32 runs on the fp32 matrix-core kernel (the vector-ALU kernel takes score modifiers and
+// slices past that kernel's 32-bit offsets); fp16/bf16 on the 16-bit matrix-core kernels: the
+// short-sequence kernel for at most 128 keys, else the tiled kernel. A 16-bit problem that
+// neither covers (a (sequence, head) slice of 1 GiB or more) is refused, never sent to
+// another kernel.
 aule_status_t dispatch(const aule::AttnProblem& p, aule_dtype_t dtype, hipStream_t stream) {
     aule::Dtype dt = static_cast<aule::Dtype>(dtype);
     hipError_t err;
     if (dt == aule::Dtype::F32)
-        err = aule::launch_attn_fwd_valu(p, dt, stream);
+        err = aule::f32_mfma_supports(p, dt) ? aule::launch_attn_fwd_f32_mfma(p, dt, stream)
+                                             : aule::launch_attn_fwd_valu(p, dt, stream);
     else if (aule::short_supports(p, dt))
         err = aule::launch_attn_fwd_short(p, dt, stream);
     else if (aule::mfma_supports(p, dt))
