@@ -46,6 +46,11 @@ BWD_SOURCES = ["tiled_attention_02_amd/csrc/attn_bwd_mfma.hip",
                "tiled_attention_02_amd/csrc/attn_mfma.h",
                "tiled_attention_02_amd/csrc/attn_device.h",
                "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
+F32_SOURCES = ["tiled_attention_02_amd/csrc/attn_fwd_f32_mfma.hip",
+               "tiled_attention_02_amd/csrc/attn_mfma.h",
+               "tiled_attention_02_amd/csrc/attn_device.h",
+               "tiled_attention_02_amd/csrc/attn_problem.h",
+               "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
 SHORT_SOURCES = ["tiled_attention_02_amd/csrc/attn_fwd_short.hip",
                  "tiled_attention_02_amd/csrc/attn_mfma.h",
                  "tiled_attention_02_amd/csrc/attn_device.h",
@@ -64,7 +69,10 @@ def kernel_source_hash(sources=KERNEL_SOURCES):
 
 
 def sources_for(workload):
-    from workloads import BWD_CONFIGS, DECODE_CONFIGS, SHORT_CONFIGS
+    from workloads import BWD_CONFIGS, CONFIGS, DECODE_CONFIGS, F32_CONFIGS, SHORT_CONFIGS
+    dense = {**CONFIGS, **F32_CONFIGS}
+    if workload in dense and dense[workload].dtype == "f32":
+        return F32_SOURCES
     if workload in DECODE_CONFIGS:
         return DECODE_SOURCES
     if workload in SHORT_CONFIGS:
@@ -385,9 +393,9 @@ def main():
     import torch
     from workloads import (BWD_CONFIGS, CONFIGS, DECODE_CONFIGS, MODS_CONFIGS, SHORT_CONFIGS,
                            BwdConfig, DecodeConfig, ModsConfig, ShortConfig)
-    from workloads import HARNESS_CONFIGS
+    from workloads import F32_CONFIGS, HARNESS_CONFIGS
     ALL = {**CONFIGS, **DECODE_CONFIGS, **BWD_CONFIGS, **MODS_CONFIGS, **SHORT_CONFIGS,
-           **HARNESS_CONFIGS}
+           **HARNESS_CONFIGS, **F32_CONFIGS}
 
     if args.copy_calibration:
         n = args.copy_calibration * (1 << 20)
@@ -441,6 +449,8 @@ def main():
         if half is not None:
             line["config"]["flops_half_convention"] = half
             line["config"]["value_half_convention"] = round(half / wall_s / 1e12, 2)
+    if cfg.dtype == "f32":
+        line["metric"] = "attention fwd TFLOPS (causal-adjusted) and % of MI355X fp32 peak"
     if isinstance(cfg, ModsConfig):
         line["metric"] = "attention varlen fwd with window/softcap/ALiBi TFLOPS (visible pairs) and % of MI355X bf16 MFMA peak"
     if isinstance(cfg, BwdConfig):

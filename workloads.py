@@ -365,6 +365,12 @@ SHORT_CONFIGS = {
                                        False, seed=7),
 }
 
+# The bf16 causal GQA shape in fp32 (the jeff.news page lists fp32 among the supported
+# dtypes): it measures the fp32 matrix-core kernel at a size that fills the GPU.
+F32_CONFIGS = {
+    "f1_f32_causal_gqa": DenseConfig("f1_f32_causal_gqa", "f32", 4, 32, 8, 4096, 128, True, seed=2),
+}
+
 # The packed-varlen benchmark harness of the ewbang.com article (its verification script's
 # comparison: batch 128, every sequence at the 4096-token maximum, 8 heads, head_dim 64,
 # fp16, non-causal): 524288 tokens, a 1.6 GB qkv pack.
