@@ -130,14 +130,26 @@ def test_bwd_training_shape_sampled():
         LSE_TOL["bf16"]
 
 
-def test_bwd_no_queries_gives_zero_kv_gradients():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_bwd_no_queries_gives_zero_kv_gradients(dtype):
     """seqlen_q = 0 against 50 keys (non-causal): dK and dV are written as zeros."""
-    k = torch.randn(1, 2, 50, 64, device="cuda", dtype=torch.bfloat16)
-    q = torch.empty(1, 4, 0, 64, device="cuda", dtype=torch.bfloat16)
+    k = torch.randn(1, 2, 50, 64, device="cuda", dtype=dtype)
+    q = torch.empty(1, 4, 0, 64, device="cuda", dtype=dtype)
     lse = torch.empty(1, 4, 0, device="cuda", dtype=torch.float32)
     dq, dk, dv = aule.flash_attention_backward(q, k, k.clone(), q, q.clone(), lse, causal=False)
     torch.cuda.synchronize()
     assert dq.numel() == 0 and bool((dk == 0).all()) and bool((dv == 0).all())
+
+
+def test_bwd_f32_matrix_core_shapes():
+    """fp32 gradients on the fp32 matrix-core kernels: head_dim 128 over several 128-key
+    blocks and 32-row tiles with ragged ends (causal and not), GQA groups of 4 and 8, cross
+    lengths both ways, a padded head_dim."""
+    check(1, 8, 2, 300, 300, 128, "f32", True, seed=81)
+    check(2, 4, 1, 200, 200, 128, "f32", False, seed=82)
+    check(1, 4, 2, 130, 270, 96, "f32", False, seed=83)
+    check(1, 4, 2, 270, 130, 128, "f32", False, seed=84)
+    check(1, 16, 2, 150, 150, 64, "f32", True, seed=85)
 
 
 def test_bwd_non_default_stream():

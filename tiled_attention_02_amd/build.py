@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libaule_attn.so")
 ARCH = "gfx950"
 
-SOURCES = ["aule_attn_api.cpp", "attn_fwd_valu.hip", "attn_fwd_f32_mfma.hip", "attn_fwd_mfma.hip", "attn_fwd_short.hip", "attn_decode.hip", "attn_decode_mfma.hip", "attn_bwd.hip",
+SOURCES = ["aule_attn_api.cpp", "attn_fwd_valu.hip", "attn_fwd_f32_mfma.hip", "attn_fwd_mfma.hip", "attn_fwd_short.hip", "attn_decode.hip", "attn_decode_mfma.hip", "attn_bwd.hip", "attn_bwd_f32_mfma.hip",
            "attn_bwd_mfma.hip"]
 
 COMMON_FLAGS = [

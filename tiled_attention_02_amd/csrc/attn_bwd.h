@@ -37,5 +37,9 @@ struct BwdProblem {
 // kernels take every dtype; the matrix-core kernels take fp16 and bf16.
 hipError_t launch_attn_bwd(const BwdProblem& p, Dtype dt, hipStream_t stream);
 hipError_t launch_attn_bwd_mfma(const BwdProblem& p, Dtype dt, hipStream_t stream);
+// fp32 on the matrix cores (full-precision fp32 products); slices past its 32-bit buffer
+// offsets stay on the vector-ALU kernels. Writes D_i = do_i . o_i into dq before dq itself.
+hipError_t launch_attn_bwd_f32_mfma(const BwdProblem& p, hipStream_t stream);
+bool bwd_f32_mfma_supports(const BwdProblem& p);
 
 }  // namespace aule

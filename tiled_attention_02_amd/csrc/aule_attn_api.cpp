@@ -47,10 +47,12 @@ aule_status_t check_common(int32_t head_dim, float scale, aule_dtype_t dtype) {
     return AULE_OK;
 }
 
-// fp16/bf16 backward on the matrix cores, fp32 on the vector ALUs
+// the backward on the matrix cores: fp16/bf16 kernels, and fp32 ones (the vector-ALU kernels
+// take fp32 slices past the fp32 kernels' 32-bit offsets)
 hipError_t launch_bwd(const aule::BwdProblem& p, aule_dtype_t dtype, hipStream_t stream) {
     const aule::Dtype dt = static_cast<aule::Dtype>(dtype);
     if (dt == aule::Dtype::F16 || dt == aule::Dtype::BF16) return aule::launch_attn_bwd_mfma(p, dt, stream);
+    if (aule::bwd_f32_mfma_supports(p)) return aule::launch_attn_bwd_f32_mfma(p, stream);
     return aule::launch_attn_bwd(p, dt, stream);
 }
 
