@@ -51,6 +51,11 @@ F32_SOURCES = ["tiled_attention_02_amd/csrc/attn_fwd_f32_mfma.hip",
                "tiled_attention_02_amd/csrc/attn_device.h",
                "tiled_attention_02_amd/csrc/attn_problem.h",
                "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
+F32_BWD_SOURCES = ["tiled_attention_02_amd/csrc/attn_bwd_f32_mfma.hip",
+                   "tiled_attention_02_amd/csrc/attn_bwd.h",
+                   "tiled_attention_02_amd/csrc/attn_mfma.h",
+                   "tiled_attention_02_amd/csrc/attn_device.h",
+                   "tiled_attention_02_amd/csrc/aule_attn_api.cpp"]
 SHORT_SOURCES = ["tiled_attention_02_amd/csrc/attn_fwd_short.hip",
                  "tiled_attention_02_amd/csrc/attn_mfma.h",
                  "tiled_attention_02_amd/csrc/attn_device.h",
@@ -78,7 +83,7 @@ def sources_for(workload):
     if workload in SHORT_CONFIGS:
         return SHORT_SOURCES
     if workload in BWD_CONFIGS:
-        return BWD_SOURCES
+        return F32_BWD_SOURCES if BWD_CONFIGS[workload].dtype == "f32" else BWD_SOURCES
     return KERNEL_SOURCES
 
 
@@ -454,7 +459,8 @@ def main():
     if isinstance(cfg, ModsConfig):
         line["metric"] = "attention varlen fwd with window/softcap/ALiBi TFLOPS (visible pairs) and % of MI355X bf16 MFMA peak"
     if isinstance(cfg, BwdConfig):
-        line["metric"] = "attention bwd TFLOPS (causal-adjusted, 2.5x forward FLOPs) and % of MI355X bf16 MFMA peak"
+        line["metric"] = ("attention bwd TFLOPS (causal-adjusted, 2.5x forward FLOPs) and % of MI355X "
+                          + ("fp32 peak" if cfg.dtype == "f32" else "bf16 MFMA peak"))
     if isinstance(cfg, DecodeConfig):
         # reading the KV cache bounds this path: throughput against the HBM roofline
         gbs = cfg.bytes_compulsory() / kern_s / 1e9

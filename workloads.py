@@ -348,6 +348,9 @@ DECODE_CONFIGS = {
 BWD_CONFIGS = {
     "b1_bf16_causal_gqa_bwd": BwdConfig("b1_bf16_causal_gqa_bwd", "bf16", 4, 32, 8, 4096, 128,
                                         True, seed=2),
+    # the same training shape in fp32
+    "b2_f32_causal_gqa_bwd": BwdConfig("b2_f32_causal_gqa_bwd", "f32", 4, 32, 8, 4096, 128,
+                                       True, seed=2),
 }
 
 # The varlen workload with all three score modifiers on: a 1024-key sliding window (causal),
