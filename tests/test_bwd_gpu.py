@@ -27,6 +27,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 GTOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
+TOL_F32_OUT = 1e-5   # the forward's fp32 bar on O
 LSE_TOL = {"f32": 2e-5, "f16": 2.0 ** -11 + 2e-5, "bf16": 2.0 ** -8 + 2e-5}
 TDT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -139,6 +140,22 @@ def test_bwd_no_queries_gives_zero_kv_gradients(dtype):
     dq, dk, dv = aule.flash_attention_backward(q, k, k.clone(), q, q.clone(), lse, causal=False)
     torch.cuda.synchronize()
     assert dq.numel() == 0 and bool((dk == 0).all()) and bool((dv == 0).all())
+
+
+def test_f32_slice_past_32bit_offsets():
+    """An fp32 (batch, head) slice of 1 GiB or more (2^21 + 32 keys at head_dim 128) is past the
+    fp32 matrix-core kernels' 32-bit buffer offsets, so the forward and the backward take the
+    vector-ALU kernels: output, LSE and gradients against the oracle."""
+    Nk = (1 << 21) + 32
+    (q, k, v, do, sc), (o, lse, dq, dk, dv) = run(1, 2, 1, 8, Nk, 128, "f32", False, seed=91)
+    assert np.max(np.abs(o - oracle.attention_ref(q, k, v, causal=False, scale=sc))) <= TOL_F32_OUT
+    ref_lse = oracle.attention_ref_lse(q, k, v, causal=False, scale=sc)
+    assert float(np.max(np.abs(lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse)))) <= LSE_TOL["f32"]
+    rdq, rdk, rdv = oracle.attention_ref_bwd(q, k, v, do, causal=False, scale=sc)
+    errs = {"dq": rel_err(dq, rdq), "dk": rel_err(dk, rdk), "dv": rel_err(dv, rdv)}
+    print("  errors", errs, flush=True)
+    for name, e in errs.items():
+        assert e <= GTOL["f32"], f"{name} relative err {e}"
 
 
 def test_bwd_f32_matrix_core_shapes():
