@@ -237,7 +237,7 @@ aule_status_t aule_attn_fwd_lse(const void* q, const void* k, const void* v, voi
  * With P = exp(scale * q k^T - lse) (masked entries 0), dV = P^T dO, dS = P * (dO v^T - D)
  * with D_i = do_i . o_i, dQ = scale * dS k and dK = scale * dS^T q; a key/value head shared
  * by several query heads (GQA) receives the sum of their gradients. fp32 arithmetic for all
- * dtypes; gradients rounded to dtype (RNE). Needs no workspace (fp32 keeps the row terms D
+ * dtypes; gradients rounded to dtype (RNE). Needs no workspace (the row terms D are kept
  * in dq until dq itself is written, in the same call); deterministic (no atomics).
  * Arguments and rules as aule_attn_fwd; the gradient buffers must not overlap any input or
  * each other. With seqlen_q == 0 and seqlen_k > 0 (non-causal) only dk and dv are read

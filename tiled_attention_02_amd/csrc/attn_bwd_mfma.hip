@@ -6,17 +6,18 @@
 // dP = do_i.v_j, dS = P (dP - D_i) with D_i = do_i.o_i; dV_j += P dO_i,
 // dK_j += scale dS q_i, dQ_i += scale dS k_j.
 //
-// Three launches, no atomics (deterministic), 32-row / 32-key steps:
+// Four launches, no atomics (deterministic), 32-row / 32-key steps:
+//   * D pre-pass: D_i = do_i . o_i (fp32) into the first 4 bytes of row i of dq, which holds
+//     it until the dQ kernel, launched last, writes dq in full.
 //   * dV pass and dK pass (one kernel, two instantiations; WV = 8 waves per workgroup at
 //     head_dim 128, 4 at 64): wave w owns 32 keys (its K rows and, for dK, its V rows held
 //     as B operands in registers) and one transposed accumulator (dV^T or dK^T, d x 32
-//     keys). The workgroup walks every query head of its GQA group and every 32-row query
-//     tile (causal: from its first key on); Q and dO tiles go through LDS, double-buffered,
-//     their global loads issued two iterations ahead. Per tile: S = Q K^T (and dP = dO V^T)
-//     with Q / dO rows fed in sigma order, so P and dS leave the accumulators already in the
-//     B-operand layout of dV^T += dO^T P and dK^T += Q^T dS, whose A operands (dO^T, Q^T)
-//     are transposing LDS reads (ds_read_b64_tr_b16). The dK pass forms D_i from the O and
-//     dO chunks as they are staged. The dV pass stages four 32-row query tiles per barrier.
+//     keys). The workgroup walks every query head of its GQA group and every query tile
+//     (causal: from its first key on); the Q and dO tiles and the rows' LSE (and D) are
+//     copied global -> LDS by the buffer unit, a tile or two ahead. Per 32-row half:
+//     S = Q K^T (and dP = dO V^T) with Q / dO rows fed in sigma order, so P and dS leave the
+//     accumulators already in the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS,
+//     whose A operands (dO^T, Q^T) are transposing LDS reads (ds_read_b64_tr_b16).
 //   * dQ (4 waves): wave w owns 32 query rows (Q and dO rows in registers, LSE_i and D_i per
 //     lane); the workgroup walks the key tiles (causal: up to its last row). Per tile:
 //     S^T = K Q^T, dP^T = V dO^T with K / V rows in sigma order, then dQ^T += K^T dS^T with
@@ -34,10 +35,11 @@ namespace aule {
 namespace {
 
 constexpr int kWaves = 4;
-// 32-row query tiles per iteration of the dV pass (one barrier per 128 rows; measured
-// 3.44 -> 3.31 -> 3.25 ms per step of the bf16 causal GQA backward for 1, 2, 4). The dK pass
-// keeps one: at 254 registers it has no room for a second score tile.
-constexpr int kDvTiles = 4;
+// 32-row query tiles per barrier and LDS buffers of the dV and dK passes, measured on the
+// bf16 causal GQA backward (B4 Hq32 Hkv8 N4096, head_dim 128): dV 2 x 2 (4 x 2, 2 x 3 and
+// 1 x 3 were 1-5% slower), dK 2 x 3 (1 x 3 was 2-3% slower).
+constexpr int kDvTiles = 2, kDvBuf = 2;
+constexpr int kDkTiles = 2, kDkBuf = 3;
 constexpr int kThreads = kWaves * 64;
 constexpr float kLog2eF = 1.4426950408889634f;
 
@@ -157,32 +159,79 @@ __device__ __forceinline__ void store_rowT(T* row, const f32x16 (&acc)[Tile<D>::
         }
 }
 
-// PASS 0 accumulates dV only (S and dV^T += dO^T P: no V, O or D needed), PASS 1 dK only
-// (S, dP and dK^T += Q^T dS). One gradient per pass halves the accumulators, so each pass
-// fits two waves per SIMD, whose matrix products then overlap the other wave's
-// exponentials; the price is S computed twice. WV waves own 32 keys each: the Q / dO / O
-// rows of the group are read once per 32 * WV keys, so wider workgroups cut that traffic.
-// QH 32-row query tiles are staged per iteration (one barrier per 32 * QH rows); within an
-// iteration the halves' products and exponentials are independent until they accumulate.
-template <typename T, int D, int PASS, int WV, int QH>
+#if defined(__HIP_DEVICE_COMPILE__)
+// One 4-byte global -> LDS copy per lane: LDS[m0 + 4 * lane] = buffer[voffset] (zero past the
+// descriptor's size); inline asm for the same reason as lds_copy16, M0 saved and restored.
+__device__ __forceinline__ void lds_copy4(i32x4 rsrc, uint32_t voffset, uint32_t lds_addr) {
+    uint32_t saved_m0;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dword %1, %2, 0 offen lds\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved_m0)
+        : "v"(voffset), "s"(rsrc), "s"(lds_addr));
+}
+#endif
+
+// D_i = do_i . o_i (fp32) into the first 4 bytes of row i of dq, which the dQ kernel writes in
+// full afterwards: 16 lanes per row, 8 dimensions each.
+template <typename T>
+__global__ __launch_bounds__(256) void attn_bwd_delta_kernel(BwdProblem p, int64_t rows) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const int sub = threadIdx.x & 15, d = p.head_dim;
+    float x = 0.f;
+    if (row < rows && sub * 8 < d) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const T*>(p.do_) + row * d + sub * 8);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const T*>(p.o) + row * d + sub * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) x = Mfma<T>::dot2(a[w], b[w], x);
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+    if (row < rows && sub == 0) *reinterpret_cast<float*>(static_cast<T*>(p.dq) + row * d) = x;
+#endif
+}
+
+// The dV pass (PASS 0: S and dV^T += dO^T P) and the dK pass (PASS 1: S, dP and
+// dK^T += Q^T dS). One gradient per pass halves the accumulators, so each pass fits two waves
+// per SIMD, whose matrix products then overlap the other wave's exponentials; the price is S
+// computed twice. WV waves own 32 keys each (K rows, and V rows for dK, held as B operands in
+// registers): the Q / dO rows of the group are read once per 32 * WV keys.
+//
+// The query tiles are copied global -> LDS by the buffer unit (buffer_load ... lds), no
+// register staging: per 32-row half, Q in the ROWS layout, dO in the COLS layout (dV) or Q in
+// the COLS and dO in the ROWS layout (dK), one 16-byte chunk per lane each, and the rows'
+// LSE (and D, from the pre-pass, in dq) as 4-byte copies. QH halves are staged per barrier;
+// NBUF buffers, the copies of tile it + NBUF - 1 issued right after the barrier that starts
+// tile it. Every wave issues the same number of copies per tile, so one explicit vmcnt per
+// tile orders them.
+template <typename T, int D, int PASS, int WV, int QH, int NBUF>
 __global__ __launch_bounds__(WV * 64) __attribute__((amdgpu_waves_per_eu(2)))
-void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
+void attn_bwd_kv_mfma_kernel(BwdProblem p) {
+#if defined(__HIP_DEVICE_COMPILE__)
     constexpr int NT = WV * 64;
-    constexpr int QR = 32 * QH;   // query rows per iteration
     using TL = Tile<D, NT>;
-    // Q (ROWS) for S; dO (COLS) for dV^T in the dV pass, (ROWS) for dP in the dK pass; Q
-    // again (COLS) for dK^T in the dK pass
-    constexpr int DO_L = PASS == 0 ? COLS : ROWS;
-    __shared__ __attribute__((aligned(16))) char sQ[2][QH][TL::BYTES];
-    __shared__ __attribute__((aligned(16))) char sdO[2][QH][TL::BYTES];
-    __shared__ __attribute__((aligned(16))) char sQc[PASS == 1 ? 2 : 1][QH][PASS == 1 ? TL::BYTES : 16];
-    __shared__ __attribute__((aligned(16))) float sL[2][QR];
-    __shared__ __attribute__((aligned(16))) float sD[2][QR];
+    static_assert(32 * TL::CPR == NT, "one 16-byte chunk per thread per tile");
+    static_assert(NBUF == 2 || NBUF == 3, "at most one later tile in flight at a barrier");
+    constexpr int QR = 32 * QH;              // query rows per tile
+    constexpr int NL = (QR + 63) / 64;       // 4-byte copies per row term (64 rows each)
+    constexpr int NCOPY = QH * (PASS == 1 ? 3 : 2) + NL * (PASS == 1 ? 2 : 1);   // per wave and tile
+    static_assert(NCOPY * (NBUF - 2) < 64, "vmcnt range");
+    __shared__ __attribute__((aligned(16))) char sQ[NBUF][QH][TL::BYTES];    // ROWS
+    __shared__ __attribute__((aligned(16))) char sdO[NBUF][QH][TL::BYTES];   // COLS (dV), ROWS (dK)
+    __shared__ __attribute__((aligned(16))) char sQc[PASS == 1 ? NBUF : 1][QH][PASS == 1 ? TL::BYTES : 16];
+    __shared__ __attribute__((aligned(16))) float sL[NBUF][64 * NL];                  // LSE
+    __shared__ __attribute__((aligned(16))) float sD[PASS == 1 ? NBUF : 1][64 * NL];  // D
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int h = lane >> 5, ln = lane & 31;
+    const int h = lane >> 5;
     const int Nq = p.seqlen_q, Nk = p.seqlen_k, d = p.head_dim, G = p.group;
+    const uint32_t rs = (uint32_t)(d * (int)sizeof(T));
     // flat grid, key blocks slowest: under causal masking block 0 walks every query tile and
     // later blocks fewer, so the longest workgroups start first; the key blocks of one
     // (batch, kv head) are heads_kv * batch apart, which keeps them on one XCD when that
@@ -191,15 +240,14 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
     const int kb = blockIdx.x / per_kb, rem = blockIdx.x - kb * per_kb;
     const int hk = rem % p.heads_kv, b = rem / p.heads_kv;
     const int j0 = kb * 32 * WV;
-    const int key = j0 + 32 * wave + ln;                 // this lane's key (B-operand column)
+    const int key = j0 + 32 * wave + (lane & 31);   // this lane's key (B-operand column)
     const int64_t kv_off = ((int64_t)b * p.heads_kv + hk) * Nk * d;
     // work: (QR-row query tile, query head g of the group), causal from the first key on.
     // The tiles are walked from the last one down, the group's heads inner, so that the
     // workgroups of one (batch, kv head) — which run on one XCD, whatever their first key —
-    // read the same Q / dO / O tile at the same time and share it through that XCD's L2
-    // (walked upwards from each block's first key, they read different rows: -2.5% time on the
-    // bf16 causal GQA backward). With no query rows (nit == 0) only the zero gradients are
-    // written: q, k, v, o, do and lse may then be null and are not read.
+    // read the same Q / dO tile at the same time and share it through that XCD's L2. With no
+    // query rows (nit == 0) only the zero gradients are written: q, k, v, o, do and lse may
+    // then be null and are not read.
     const int i_start = p.causal ? j0 : 0;
     const int ntile = Nq > i_start ? (Nq - i_start + QR - 1) / QR : 0;
     const int nit = G * ntile;
@@ -209,163 +257,156 @@ void attn_bwd_dkdv_mfma_kernel(BwdProblem p) {
         fetch_operand<T, D>(kf, static_cast<const T*>(p.k) + kv_off, key, Nk, d, h);
         if constexpr (PASS == 1) fetch_operand<T, D>(vf, static_cast<const T*>(p.v) + kv_off, key, Nk, d, h);
     }
-
     f32x16 acc[TL::DB];   // dV^T (PASS 0) or dK^T (PASS 1)
 #pragma unroll
     for (int db = 0; db < TL::DB; ++db) acc[db] = f32x16{};
     const float c2 = p.scale * kLog2eF;
 
-    // Register staging of one query tile's global loads. Two sets: tile it + 2 is fetched
-    // into the set that held tile it while tile it + 1 (fetched an iteration earlier) is
-    // committed to LDS, so each load has two iterations to arrive.
-    struct Stage {
-        u32x4 q[QH][TL::NCH], dO[QH][TL::NCH], o[QH][PASS == 1 ? TL::NCH : 1];
-        float lse;
+    // this lane's chunk of a tile in each layout: slot wave * 64 + lane of the LDS image
+    // holds chunk slot % CPR of row slot / CPR, which is global chunk (slot % CPR) ^ swz(row)
+    uint32_t off_rows, off_cols;
+    {
+        const int slot = wave * 64 + lane;
+        const int row = slot / TL::CPR, pc = slot % TL::CPR;
+        const int cr = pc ^ swz<D, ROWS>(row), cc = pc ^ swz<D, COLS>(row);
+        off_rows = cr * 8 < d ? row * rs + cr * 16 : kOobOffset;
+        off_cols = cc * 8 < d ? row * rs + cc * 16 : kOobOffset;
+    }
+    const uint32_t off_q = off_rows, off_do = PASS == 0 ? off_cols : off_rows;
+    auto lds_addr = [](const void* q) { return (uint32_t)(uintptr_t)(lds_void*)q; };
+    auto tile_of = [&](int it, int& i0, int64_t& bh) {
+        const int tr = it / G, g = it - tr * G;
+        i0 = i_start + QR * (ntile - 1 - tr);
+        bh = (int64_t)b * p.heads_q + (int64_t)hk * G + g;
     };
-    // (tile counted from the last, head) of the next fetch and of the current body: advanced
-    // one step per iteration instead of dividing the iteration index by the group size
-    int f_tr = 0, f_g = 0, b_tr = 0, b_g = 0;
-    auto step = [&](int& tr, int& g) {
-        if (++g == G) { g = 0; ++tr; }
-    };
-    const int64_t bh0 = (int64_t)b * p.heads_q + (int64_t)hk * G;
-    auto fetch = [&](Stage& st) {
-        const int i0 = i_start + QR * (ntile - 1 - f_tr);
-        const int64_t bh = bh0 + f_g;
+    auto issue = [&](int it, int buf) {
+        int i0;
+        int64_t bh;
+        tile_of(it, i0, bh);
         const int64_t q_off = bh * Nq * d;
-        step(f_tr, f_g);
-        const __amdgpu_buffer_rsrc_t rq = slice_rsrc(static_cast<const T*>(p.q) + q_off, Nq, d);
-        const __amdgpu_buffer_rsrc_t rdo = slice_rsrc(static_cast<const T*>(p.do_) + q_off, Nq, d);
+        const int nb = Nq * (int)rs;
+        const i32x4 rq = buffer_desc(static_cast<const T*>(p.q) + q_off, nb);
+        const i32x4 rdo = buffer_desc(static_cast<const T*>(p.do_) + q_off, nb);
+        const uint32_t slot = (uint32_t)wave * 1024u;
 #pragma unroll
         for (int hf = 0; hf < QH; ++hf) {
-            fetch_rows_buf<T, D, NT>(st.q[hf], rq, i0 + 32 * hf, d);
-            fetch_rows_buf<T, D, NT>(st.dO[hf], rdo, i0 + 32 * hf, d);
+            const uint32_t base = (uint32_t)(i0 + 32 * hf) * rs;
+            lds_copy16(rq, off_q + base, __builtin_amdgcn_readfirstlane(lds_addr(sQ[buf][hf]) + slot));
             if constexpr (PASS == 1)
-                fetch_rows_buf<T, D, NT>(st.o[hf], slice_rsrc(static_cast<const T*>(p.o) + q_off, Nq, d), i0 + 32 * hf, d);
+                lds_copy16(rq, off_cols + base, __builtin_amdgcn_readfirstlane(lds_addr(sQc[buf][hf]) + slot));
+            lds_copy16(rdo, off_do + base, __builtin_amdgcn_readfirstlane(lds_addr(sdO[buf][hf]) + slot));
         }
-        // every thread loads (rows past the end read as zero); the first QR are committed
-        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.lse) + bh * Nq, (short)0, Nq * 4, (int)kBufferFlags);
-        const uint32_t loff = (int)threadIdx.x < QR ? (uint32_t)(i0 + (int)threadIdx.x) * 4u : kOobOffset;
-        st.lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, (int)loff, 0, 0));
-    };
-    auto commit = [&](int buf, const Stage& st) {
+        // every wave copies the same row terms (identical bytes), which keeps the copy count
+        // uniform across waves; rows past the tile or the sequence read as zero
+        const i32x4 rl = buffer_desc(p.lse + bh * Nq, Nq * 4);
 #pragma unroll
-        for (int hf = 0; hf < QH; ++hf) {
-            put_rows<D, ROWS, NT>(sQ[buf][hf], st.q[hf]);
-            put_rows<D, DO_L, NT>(sdO[buf][hf], st.dO[hf]);
-            if constexpr (PASS == 1) put_rows<D, COLS, NT>(sQc[buf][hf], st.q[hf]);
-            // D_i = do_i . o_i: a chunk pair per thread, summed over the CPR chunks of a row
-            // (consecutive lanes)
-            if constexpr (PASS == 1)
+        for (int c = 0; c < NL; ++c) {
+            const int r = 64 * c + lane;
+            lds_copy4(rl, r < QR ? (uint32_t)(i0 + r) * 4u : kOobOffset,
+                      __builtin_amdgcn_readfirstlane(lds_addr(&sL[buf][64 * c])));
+        }
+        if constexpr (PASS == 1) {
+            const i32x4 rd = buffer_desc(static_cast<const T*>(p.dq) + q_off, nb);
 #pragma unroll
-            for (int i = 0; i < TL::NCH; ++i) {
-                float x = 0.f;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) x = Mfma<T>::dot2(st.dO[hf][i][w], st.o[hf][i][w], x);
-#pragma unroll
-                for (int off = 1; off < TL::CPR; off <<= 1) x += __shfl_xor(x, off);
-                const int idx = (int)threadIdx.x + NT * i;
-                if (idx % TL::CPR == 0) sD[buf][32 * hf + idx / TL::CPR] = -x;   // -D
+            for (int c = 0; c < NL; ++c) {
+                const int r = 64 * c + lane;
+                lds_copy4(rd, r < QR ? (uint32_t)(i0 + r) * rs : kOobOffset,
+                          __builtin_amdgcn_readfirstlane(lds_addr(&sD[buf][64 * c])));
             }
         }
-        if ((int)threadIdx.x < QR) sL[buf][threadIdx.x] = st.lse * kLog2eF;
     };
 
     const int kw0 = j0 + 32 * wave;   // this wave's first key
-    auto body = [&](int it, Stage& mine, const Stage& other) {
-        const int buf = it & 1;
-        const int i0q = i_start + QR * (ntile - 1 - b_tr);
-        step(b_tr, b_g);
-        if (it + 2 < nit) fetch(mine);
+    auto body = [&](int it, int buf) {
+        // tile it landed everywhere (the copies of the NBUF - 2 later tiles may still be in
+        // flight) and every wave is past tile it - 1, whose buffer takes tile it + NBUF - 1
+        if (NBUF > 2 && it + 1 < nit) {
+            constexpr int n = NCOPY * (NBUF - 2);
+            __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));   // vmcnt(n) lgkmcnt(0)
+        } else {
+            __builtin_amdgcn_s_waitcnt(7 << 4);                                   // vmcnt(0) lgkmcnt(0)
+        }
+        asm volatile("s_barrier" ::: "memory");
+        if (it + NBUF - 1 < nit) issue(it + NBUF - 1, (buf + NBUF - 1) % NBUF);
+        int i0q;
+        int64_t bh;
+        tile_of(it, i0q, bh);
 #pragma unroll
         for (int hf = 0; hf < QH; ++hf) {
-        const int i0 = i0q + 32 * hf;
-        // S = Q K^T, dP - D = dO V^T - D: register r holds query i0 + 16(r/8) + 8h + r%8, key
-        // `key`; the dP accumulator starts from -D of its rows (two runs of 8 consecutive rows,
-        // 16-byte reads), so dS = P (dP - D) needs no further registers
-        f32x16 s = f32x16{}, dp = f32x16{};
-        if constexpr (PASS == 1) {
+            const int i0 = i0q + 32 * hf;
+            // S = Q K^T, dP - D = dO V^T - D: register r holds query i0 + 16(r/8) + 8h + r%8,
+            // key `key`; the dP accumulator starts from -D of its rows (two runs of 8
+            // consecutive rows, 16-byte reads), so dS = P (dP - D) needs no further registers
+            f32x16 s = f32x16{}, dp = f32x16{};
+            if constexpr (PASS == 1) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const float4* pd = reinterpret_cast<const float4*>(&sD[buf][32 * hf + 16 * kk + 8 * h]);
-                const float4 x = pd[0], y = pd[1];
-                dp[8 * kk + 0] = x.x; dp[8 * kk + 1] = x.y; dp[8 * kk + 2] = x.z; dp[8 * kk + 3] = x.w;
-                dp[8 * kk + 4] = y.x; dp[8 * kk + 5] = y.y; dp[8 * kk + 6] = y.z; dp[8 * kk + 7] = y.w;
+                for (int kk = 0; kk < 2; ++kk) {
+                    const float4* pd = reinterpret_cast<const float4*>(&sD[buf][32 * hf + 16 * kk + 8 * h]);
+                    const float4 x = pd[0], y = pd[1];
+                    dp[8 * kk + 0] = -x.x; dp[8 * kk + 1] = -x.y; dp[8 * kk + 2] = -x.z; dp[8 * kk + 3] = -x.w;
+                    dp[8 * kk + 4] = -y.x; dp[8 * kk + 5] = -y.y; dp[8 * kk + 6] = -y.z; dp[8 * kk + 7] = -y.w;
+                }
             }
-        }
 #pragma unroll
-        for (int ks = 0; ks < TL::KS; ++ks) {
-            s = Mfma<T>::mma(rd_rows<D>(sQ[buf][hf], ks, lane), kf[ks], s);
-            if constexpr (PASS == 1) dp = Mfma<T>::mma(rd_rows<D>(sdO[buf][hf], ks, lane), vf[ks], dp);
-        }
-        // P (and dS) packed to 16 bit. The row statistics of each run of 8 consecutive query
-        // rows are read as two 16-byte vectors. Tiles away from the diagonal and the ends need
-        // no mask: a uniform branch picks the mask-free form; on edge tiles every exponential
-        // is taken and masked pairs are selected to 0 (no per-element branch).
-        u32x4 pf[2], dsf[2];
-        auto p_ds = [&](auto masked) {
+            for (int ks = 0; ks < TL::KS; ++ks) {
+                s = Mfma<T>::mma(rd_rows<D>(sQ[buf][hf], ks, lane), kf[ks], s);
+                if constexpr (PASS == 1) dp = Mfma<T>::mma(rd_rows<D>(sdO[buf][hf], ks, lane), vf[ks], dp);
+            }
+            // P (dV) or dS (dK) packed to 16 bit. The LSE of each run of 8 consecutive query
+            // rows is read as two 16-byte vectors. Tiles away from the diagonal and the ends
+            // need no mask: a uniform branch picks the mask-free form; on edge tiles every
+            // exponential is taken and masked pairs are selected to 0 (no per-element branch).
+            u32x4 bf[2];
+            auto p_ds = [&](auto masked) {
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int q0 = 16 * kk + 8 * h;
-                float lq[8];
-                {
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int q0 = 16 * kk + 8 * h;
                     const float4* pl = reinterpret_cast<const float4*>(&sL[buf][32 * hf + q0]);
                     const float4 a = pl[0], c = pl[1];
-                    lq[0] = a.x; lq[1] = a.y; lq[2] = a.z; lq[3] = a.w;
-                    lq[4] = c.x; lq[5] = c.y; lq[6] = c.z; lq[7] = c.w;
-                }
-                float pv[8], dsv[8];
+                    const float lq[8] = {a.x * kLog2eF, a.y * kLog2eF, a.z * kLog2eF, a.w * kLog2eF,
+                                         c.x * kLog2eF, c.y * kLog2eF, c.z * kLog2eF, c.w * kLog2eF};
+                    float v[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float x = fmaf(s[8 * kk + e], c2, -lq[e]);
-                    if constexpr (decltype(masked)::value) {
-                        const int qi = i0 + q0 + e;
-                        const bool vis = qi < Nq && key < Nk && (!p.causal || key <= qi);
-                        x = vis ? x : -INFINITY;   // exp2(-inf) = +0
+                    for (int e = 0; e < 8; ++e) {
+                        float x = fmaf(s[8 * kk + e], c2, -lq[e]);
+                        if constexpr (decltype(masked)::value) {
+                            const int qi = i0 + q0 + e;
+                            const bool vis = qi < Nq && key < Nk && (!p.causal || key <= qi);
+                            x = vis ? x : -INFINITY;   // exp2(-inf) = +0
+                        }
+                        const float pe = __builtin_amdgcn_exp2f(x);
+                        v[e] = PASS == 1 ? pe * dp[8 * kk + e] : pe;
                     }
-                    const float pe = __builtin_amdgcn_exp2f(x);
-                    pv[e] = pe;
-                    dsv[e] = PASS == 1 ? pe * dp[8 * kk + e] : 0.f;
+                    bf[kk] = u32x4{Mfma<T>::pack2(v[0], v[1]), Mfma<T>::pack2(v[2], v[3]),
+                                   Mfma<T>::pack2(v[4], v[5]), Mfma<T>::pack2(v[6], v[7])};
                 }
-                if constexpr (PASS == 0)
-                    pf[kk] = u32x4{Mfma<T>::pack2(pv[0], pv[1]), Mfma<T>::pack2(pv[2], pv[3]),
-                                   Mfma<T>::pack2(pv[4], pv[5]), Mfma<T>::pack2(pv[6], pv[7])};
-                else
-                    dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
-                                    Mfma<T>::pack2(dsv[4], dsv[5]), Mfma<T>::pack2(dsv[6], dsv[7])};
-            }
-        };
-        const bool inner = i0 + 32 <= Nq && kw0 + 32 <= Nk && (!p.causal || kw0 + 31 <= i0);
-        if (inner) p_ds(std::false_type{});
-        else p_ds(std::true_type{});
-        // dV^T += dO^T P (PASS 0) or dK^T += Q^T dS (PASS 1)
+            };
+            const bool inner = i0 + 32 <= Nq && kw0 + 32 <= Nk && (!p.causal || kw0 + 31 <= i0);
+            if (inner) p_ds(std::false_type{});
+            else p_ds(std::true_type{});
+            // dV^T += dO^T P (PASS 0) or dK^T += Q^T dS (PASS 1)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int db = 0; db < TL::DB; ++db) {
-                if constexpr (PASS == 0) acc[db] = Mfma<T>::mma(rd_cols<D>(sdO[buf][hf], db, kk, lane), pf[kk], acc[db]);
-                else acc[db] = Mfma<T>::mma(rd_cols<D>(sQc[buf][hf], db, kk, lane), dsf[kk], acc[db]);
-            }
+                for (int db = 0; db < TL::DB; ++db) {
+                    if constexpr (PASS == 0) acc[db] = Mfma<T>::mma(rd_cols<D>(sdO[buf][hf], db, kk, lane), bf[kk], acc[db]);
+                    else acc[db] = Mfma<T>::mma(rd_cols<D>(sQc[buf][hf], db, kk, lane), bf[kk], acc[db]);
+                }
         }
-        if (it + 1 < nit) commit(buf ^ 1, other);
-        __syncthreads();
     };
-
-    Stage st0, st1;
-    if (nit > 0) {
-        fetch(st0);
-        commit(0, st0);
-    }
-    if (nit > 1) fetch(st1);
-    __syncthreads();
-    for (int it = 0; it < nit; it += 2) {
-        body(it, st0, st1);
-        if (it + 1 < nit) body(it + 1, st1, st0);
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+        if (t < nit) issue(t, t);
+    for (int it = 0; it < nit; it += NBUF) {
+#pragma unroll
+        for (int t = 0; t < NBUF; ++t)
+            if (it + t < nit) body(it + t, t);
     }
     if (key < Nk) {
         if constexpr (PASS == 1) store_rowT<T, D>(static_cast<T*>(p.dk) + kv_off + (int64_t)key * d, acc, p.scale, d, h);
         else store_rowT<T, D>(static_cast<T*>(p.dv) + kv_off + (int64_t)key * d, acc, 1.f, d, h);
     }
+#endif
 }
 
 template <typename T, int D>
@@ -505,11 +546,18 @@ hipError_t launch_typed(const BwdProblem& p, hipStream_t stream) {
     const int64_t nk = (int64_t)((p.seqlen_k + RK - 1) / RK) * p.heads_kv * p.batch;
     const int64_t nq = (int64_t)((p.seqlen_q + R - 1) / R) * p.heads_q * p.batch;
     if (nk > INT32_MAX || nq > INT32_MAX) return hipErrorInvalidConfiguration;
+    const int64_t rows = (int64_t)p.batch * p.heads_q * p.seqlen_q;
+    if ((rows + 15) / 16 > INT32_MAX) return hipErrorInvalidConfiguration;
+    hipError_t e;
+    if (rows > 0) {   // D into the rows of dq, before the dK pass reads it
+        hipLaunchKernelGGL(attn_bwd_delta_kernel<T>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, p, rows);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     dim3 gk((unsigned)nk);
-    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 0, WV, kDvTiles>), gk, dim3(WV * 64), 0, stream, p);
-    hipError_t e = hipGetLastError();
+    hipLaunchKernelGGL((attn_bwd_kv_mfma_kernel<T, D, 0, WV, kDvTiles, kDvBuf>), gk, dim3(WV * 64), 0, stream, p);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_dkdv_mfma_kernel<T, D, 1, WV, 1>), gk, dim3(WV * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_kv_mfma_kernel<T, D, 1, WV, kDkTiles, kDkBuf>), gk, dim3(WV * 64), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess || p.seqlen_q == 0) return e;   // no query rows: dK = dV = 0, no dQ
     dim3 gq((unsigned)nq);
