@@ -9,21 +9,23 @@
 // Four launches, no atomics (deterministic), 32-row / 32-key steps:
 //   * D pre-pass: D_i = do_i . o_i (fp32) into the first 4 bytes of row i of dq, which holds
 //     it until the dQ kernel, launched last, writes dq in full.
-//   * dV pass and dK pass (one kernel, two instantiations; WV = 8 waves per workgroup at
-//     head_dim 128, 4 at 64): wave w owns 32 keys (its K rows and, for dK, its V rows held
-//     as B operands in registers) and one transposed accumulator (dV^T or dK^T, d x 32
-//     keys). The workgroup walks every query head of its GQA group and every query tile
-//     (causal: from its first key on); the Q and dO tiles and the rows' LSE (and D) are
-//     copied global -> LDS by the buffer unit, a tile or two ahead. Per 32-row half:
-//     S = Q K^T (and dP = dO V^T) with Q / dO rows fed in sigma order, so P and dS leave the
-//     accumulators already in the B-operand layout of dV^T += dO^T P and dK^T += Q^T dS,
-//     whose A operands (dO^T, Q^T) are transposing LDS reads (ds_read_b64_tr_b16).
-//   * dQ (4 waves): wave w owns 32 query rows (Q and dO rows in registers, LSE_i and D_i per
-//     lane); the workgroup walks the key tiles (causal: up to its last row). Per tile:
+//   * dV pass and dK pass (one kernel, two instantiations) and dQ, each with WV = 8 waves per
+//     workgroup at head_dim 128, 4 at 64.
+//   * dV / dK pass: wave w owns 32 keys (its K rows and, for dK, its V rows held as B operands
+//     in registers) and one transposed accumulator (dV^T or dK^T, d x 32 keys). The workgroup
+//     walks every query head of its GQA group and every query tile (causal: from its first
+//     key on). Per 32-row half: S = Q K^T (and dP = dO V^T) with Q / dO rows fed in sigma
+//     order, so P and dS leave the accumulators already in the B-operand layout of
+//     dV^T += dO^T P and dK^T += Q^T dS, whose A operands (dO^T, Q^T) are transposing LDS
+//     reads (ds_read_b64_tr_b16).
+//   * dQ: wave w owns 32 query rows (Q and dO rows in registers, LSE_i and D_i per lane); the
+//     workgroup walks the key tiles (causal: up to its last row). Per 32-key half:
 //     S^T = K Q^T, dP^T = V dO^T with K / V rows in sigma order, then dQ^T += K^T dS^T with
 //     K^T read transposed from LDS.
-// The dQ kernel keeps K / V tiles row-major [32][D] with one 16-byte pad per row; the dK / dV
-// passes store each staged tile XOR-swizzled in the layout of the read that uses it.
+// Every staged tile (Q and dO, or K and V) is copied global -> LDS by the buffer unit, in the
+// XOR-swizzled layout of the read that uses it (twice when it is read both ways), two 32-row
+// halves per barrier, double-buffered: the next tile's copies are issued right after the
+// barrier that starts a tile.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -34,95 +36,55 @@
 namespace aule {
 namespace {
 
-constexpr int kWaves = 4;
-// 32-row query tiles per barrier and LDS buffers of the dV and dK passes, measured on the
-// bf16 causal GQA backward (B4 Hq32 Hkv8 N4096, head_dim 128): dV 2 x 2 (4 x 2, 2 x 3 and
-// 1 x 3 were 1-5% slower), dK 2 x 3 (1 x 3 was 2-3% slower).
-constexpr int kDvTiles = 2, kDvBuf = 2;
-constexpr int kDkTiles = 2, kDkBuf = 3;
-constexpr int kThreads = kWaves * 64;
+// 32-row query tiles (dV, dK) or 32-key tiles (dQ) per barrier, and LDS buffers, measured on
+// the bf16 causal GQA backward (B4 Hq32 Hkv8 N4096, head_dim 128, and the same at 64): two
+// tiles, double-buffered, in all three (four tiles, triple buffering or one tile per barrier
+// were 1-5% slower at head_dim 128; the triple-buffered dK pass 7% slower at 64).
+constexpr int kTiles = 2, kBufs = 2;
 constexpr float kLog2eF = 1.4426950408889634f;
 
-template <int D, int NT = kThreads>
+template <int D>
 struct Tile {
-    static constexpr int RS = D * 2;                      // bytes per LDS row (swizzled layouts)
-    static constexpr int RSP = D * 2 + 16;                // bytes per LDS row (PAD layout)
+    static constexpr int RS = D * 2;                      // bytes per LDS row
     static constexpr int CPR = D / 8;                     // 16-byte chunks per row
-    static constexpr int BYTES = 32 * RS;
-    static constexpr int BYTESP = 32 * RSP;
-    static constexpr int NCH = 32 * CPR / NT;             // chunks per thread per tile
+    static constexpr int BYTES = 32 * RS;                 // one 32-row tile
     static constexpr int KS = D / 16;                     // k-steps over head_dim
     static constexpr int DB = D / 32;                     // 32-row blocks of head_dim
-    static_assert(NCH >= 1 && NCH * NT == 32 * CPR, "tile chunks must split evenly");
 };
 
-// Rows [r0, r0 + 32) of a [rows, d] slice as 16-byte chunks, this thread's share, through a
-// buffer resource covering exactly the slice: rows past the end read as zero (the hardware's
-// range check) and chunks past head_dim are sent past the range, so there is no branch and no
-// zero fill (with those, the compiler waited for every load in flight before refilling a
-// staging set, which undid the two-deep staging).
-template <typename T, int D, int NT = kThreads>
-__device__ __forceinline__ void fetch_rows_buf(u32x4 (&c)[(Tile<D, NT>::NCH)], __amdgpu_buffer_rsrc_t rs, int r0, int d) {
-#pragma unroll
-    for (int i = 0; i < Tile<D, NT>::NCH; ++i) {
-        const int idx = (int)threadIdx.x + NT * i;
-        const int row = idx / Tile<D>::CPR, ch = idx % Tile<D>::CPR;
-        const uint32_t off = ch * 8 < d ? (uint32_t)(r0 + row) * (uint32_t)(d * (int)sizeof(T)) + (uint32_t)ch * 16u : kOobOffset;
-        c[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0));
-    }
-}
-// Resource for a [rows, d] slice of T (at most 1 GiB, checked by the host).
-template <typename T>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slice_rsrc(const T* base, int rows, int d) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, rows > 0 ? rows * d * (int)sizeof(T) : 0,
-                                             (int)kBufferFlags);
-}
 // Two LDS layouts of a 32-row tile, one per read pattern, with the XOR swizzles of the
 // forward kernel's K and V tiles (chunk c of row r stored at chunk c ^ swz(r)):
 //   ROWS: rd_rows reads one chunk of rows sigma(0..31) per instruction -> kswz;
 //   COLS: rd_cols reads 4 consecutive rows x 2 neighbouring chunks per 16 lanes -> vswz.
-// A tile read both ways is stored twice. PAD: unswizzled rows padded by 16 bytes, read both
-// ways from one copy (the transposed reads then conflict 2-way; the dQ kernel keeps it, where
-// a second copy of K cost more than the conflicts).
-enum Layout { ROWS = 0, COLS = 1, PAD = 2 };
+// A tile read both ways is stored twice.
+enum Layout { ROWS = 0, COLS = 1 };
 template <int D, int L>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (L == ROWS) return kswz<D / 8>(row);
-    else if constexpr (L == COLS) return vswz<D / 8>(row);
-    else return 0;
-}
-template <int D, int L> constexpr int row_bytes() { return L == PAD ? Tile<D>::RSP : Tile<D>::RS; }
-template <int D, int L, int NT = kThreads>
-__device__ __forceinline__ void put_rows(char* tile, const u32x4 (&c)[(Tile<D, NT>::NCH)]) {
-#pragma unroll
-    for (int i = 0; i < Tile<D, NT>::NCH; ++i) {
-        const int idx = (int)threadIdx.x + NT * i;
-        const int row = idx / Tile<D>::CPR, ch = idx % Tile<D>::CPR;
-        *reinterpret_cast<u32x4*>(tile + row * row_bytes<D, L>() + (ch ^ swz<D, L>(row)) * 16) = c[i];
-    }
+    else return vswz<D / 8>(row);
 }
 
 // A operand with rows in sigma order from a ROWS tile: lane l supplies row sigma(l % 32),
 // k-chunk 2ks + h (stored at chunk (2ks + h) ^ kswz(sigma(l % 32)) = (2ks + h) ^ kx_lane(l % 32)).
-template <int D, int L = ROWS>
+template <int D>
 __device__ __forceinline__ u32x4 rd_rows(const char* tile, int ks, int lane) {
     const int l32 = lane & 31;
-    const int x = L == PAD ? 0 : kx_lane<Tile<D>::CPR>(l32);
-    return *reinterpret_cast<const u32x4*>(tile + sigma(l32) * row_bytes<D, L>() + (((2 * ks + (lane >> 5)) ^ x) * 16));
+    const int x = kx_lane<Tile<D>::CPR>(l32);
+    return *reinterpret_cast<const u32x4*>(tile + sigma(l32) * Tile<D>::RS + (((2 * ks + (lane >> 5)) ^ x) * 16));
 }
 // A operand of a transposed COLS tile: A[m = column 32db + l % 32][k = row 16kk + 8h .. + 7],
 // two transposing 8-byte reads (each 16-lane group reads 4 rows x 16 columns); vswz depends
 // on the row modulo 4 only, the same for both reads.
-template <int D, int L = COLS>
+template <int D>
 __device__ __forceinline__ u32x4 rd_cols(const char* tile, int db, int kk, int lane) {
     const int tg = lane >> 4, tc = lane & 15;
     const int row0 = 16 * kk + 8 * (tg >> 1) + (tc >> 2);
-    const int x = L == PAD ? 0 : vswz<D / 8>(row0);
+    const int x = vswz<D / 8>(row0);
     const int coff = ((4 * db + 2 * (tg & 1) + ((tc & 3) >> 1)) ^ x) * 16 + (tc & 1) * 8;
     u32x4 out;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-        const char* addr = tile + (row0 + 4 * t) * row_bytes<D, L>() + coff;
+        const char* addr = tile + (row0 + 4 * t) * Tile<D>::RS + coff;
         const i16x4_t part = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<char*>(addr)));
         const u32x2 w = __builtin_bit_cast(u32x2, part);
         out[2 * t] = w[0];
@@ -214,7 +176,7 @@ __global__ __launch_bounds__(WV * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_kv_mfma_kernel(BwdProblem p) {
 #if defined(__HIP_DEVICE_COMPILE__)
     constexpr int NT = WV * 64;
-    using TL = Tile<D, NT>;
+    using TL = Tile<D>;
     static_assert(32 * TL::CPR == NT, "one 16-byte chunk per thread per tile");
     static_assert(NBUF == 2 || NBUF == 3, "at most one later tile in flight at a barrier");
     constexpr int QR = 32 * QH;              // query rows per tile
@@ -409,52 +371,57 @@ void attn_bwd_kv_mfma_kernel(BwdProblem p) {
 #endif
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+// dQ: wave w owns 32 query rows (its Q and dO rows held as B operands in registers, LSE_i and
+// D_i per lane, D from the pre-pass) and one transposed accumulator dQ^T (d x 32 queries); the
+// workgroup walks the key tiles (causal: up to its last row). The K and V tiles are copied
+// global -> LDS by the buffer unit: per 32-key half, K in the ROWS and the COLS layout and V in
+// the ROWS layout, one 16-byte chunk per lane each; KH halves per barrier, NBUF buffers, the
+// copies of tile t + NBUF - 1 issued right after the barrier that starts tile t. Per half:
+// S^T = K Q^T, dP^T = V dO^T with K / V rows in sigma order, then dQ^T += K^T dS^T with K^T
+// read transposed; a wave skips the halves that lie wholly past its rows.
+template <typename T, int D, int WQ, int KH, int NBUF>
+__global__ __launch_bounds__(WQ * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_bwd_dq_mfma_kernel(BwdProblem p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    constexpr int NT = WQ * 64;
     using TL = Tile<D>;
-    // K and V tiles in the PAD layout (K read both ways from one copy)
-    __shared__ __attribute__((aligned(16))) char sK[2][TL::BYTESP];
-    __shared__ __attribute__((aligned(16))) char sV[2][TL::BYTESP];
+    static_assert(32 * TL::CPR == NT, "one 16-byte chunk per thread per tile");
+    static_assert(NBUF == 2 || NBUF == 3, "at most one later tile in flight at a barrier");
+    constexpr int KR = 32 * KH;        // keys per tile
+    constexpr int NCOPY = 3 * KH;      // copies per wave and tile
+    __shared__ __attribute__((aligned(16))) char sK[NBUF][KH][TL::BYTES];    // ROWS
+    __shared__ __attribute__((aligned(16))) char sKc[NBUF][KH][TL::BYTES];   // COLS
+    __shared__ __attribute__((aligned(16))) char sV[NBUF][KH][TL::BYTES];    // ROWS
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int h = lane >> 5, ln = lane & 31;
+    const int h = lane >> 5;
     const int Nq = p.seqlen_q, Nk = p.seqlen_k, d = p.head_dim;
+    const uint32_t rs = (uint32_t)(d * (int)sizeof(T));
     // flat grid, query blocks slowest and (causal) last block first: the longest walks start
     // first. Within a block index the G query heads of one (batch, kv head) are
     // batch * heads_kv apart, which puts them on one XCD (sharing its L2 copy of that K/V)
     // when that count is a multiple of 8.
     const int per_qb = p.heads_q * p.batch;
     const int t_ = blockIdx.x / per_qb, rem = blockIdx.x - t_ * per_qb;
-    const int nqb = (Nq + 32 * kWaves - 1) / (32 * kWaves);
+    const int nqb = (Nq + 32 * WQ - 1) / (32 * WQ);
     const int qblk = p.causal ? nqb - 1 - t_ : t_;
     const int nkvu = p.batch * p.heads_kv;
     const int gi = rem / nkvu, u = rem - gi * nkvu;
     const int b = u / p.heads_kv, hq = (u - b * p.heads_kv) * p.group + gi;
-    const int i0 = qblk * 32 * kWaves;
+    const int i0 = qblk * 32 * WQ;
     const int hk = hq / p.group;
-    const int qi = i0 + 32 * wave + ln;                  // this lane's query (B-operand column)
+    const int qw0 = i0 + 32 * wave;                      // this wave's first query row
+    const int qi = qw0 + (lane & 31);                    // this lane's query (B-operand column)
     const int64_t bh = (int64_t)b * p.heads_q + hq;
     const int64_t q_off = bh * Nq * d;
     const int64_t kv_off = ((int64_t)b * p.heads_kv + hk) * Nk * d;
-    const T* Kb = static_cast<const T*>(p.k) + kv_off;
-    const T* Vb = static_cast<const T*>(p.v) + kv_off;
 
     u32x4 qf[TL::KS], dof[TL::KS];
     fetch_operand<T, D>(qf, static_cast<const T*>(p.q) + q_off, qi, Nq, d, h);
     fetch_operand<T, D>(dof, static_cast<const T*>(p.do_) + q_off, qi, Nq, d, h);
-    float delta;
-    {
-        u32x4 of[TL::KS];
-        fetch_operand<T, D>(of, static_cast<const T*>(p.o) + q_off, qi, Nq, d, h);
-        float x = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < TL::KS; ++ks)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) x = Mfma<T>::dot2(dof[ks][w], of[ks][w], x);
-        delta = x + __shfl_xor(x, 32);                    // the other half of the row
-    }
+    // D_i sits in the first 4 bytes of row i of dq until this kernel writes the row
+    const float delta = qi < Nq ? *reinterpret_cast<const float*>(static_cast<const T*>(p.dq) + q_off + (int64_t)qi * d) : 0.f;
     const float lse2 = qi < Nq ? p.lse[bh * Nq + qi] * kLog2eF : 0.f;
     const float c2 = p.scale * kLog2eF;
 
@@ -462,87 +429,107 @@ void attn_bwd_dq_mfma_kernel(BwdProblem p) {
 #pragma unroll
     for (int db = 0; db < TL::DB; ++db) dq[db] = f32x16{};
 
-    const int j_end = p.causal ? min(Nk, i0 + 32 * kWaves) : Nk;
-    const int nkt = (j_end + 31) / 32;
-    // two register staging sets, as in the dK / dV kernel: key tile t + 2 is fetched while
-    // tile t + 1 (fetched an iteration earlier) is committed to LDS
-    struct Stage { u32x4 k[TL::NCH], v[TL::NCH]; };
-    const __amdgpu_buffer_rsrc_t rk = slice_rsrc(Kb, Nk, d), rv = slice_rsrc(Vb, Nk, d);
-    auto fetch = [&](int t, Stage& st) {
-        fetch_rows_buf<T, D>(st.k, rk, 32 * t, d);
-        fetch_rows_buf<T, D>(st.v, rv, 32 * t, d);
-    };
-    auto commit = [&](int buf, const Stage& st) {
-        put_rows<D, PAD>(sK[buf], st.k);
-        put_rows<D, PAD>(sV[buf], st.v);
-    };
-    const int qw0 = i0 + 32 * wave;   // this wave's first query row
-    auto body = [&](int t, Stage& mine, const Stage& other) {
-        const int buf = t & 1;
-        if (t + 2 < nkt) fetch(t + 2, mine);
-        // S^T = K Q^T, dP^T = V dO^T: register r holds key 32t + 16(r/8) + 8h + r%8, query qi
-        f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < TL::KS; ++ks) {
-            s = Mfma<T>::mma(rd_rows<D, PAD>(sK[buf], ks, lane), qf[ks], s);
-            dp = Mfma<T>::mma(rd_rows<D, PAD>(sV[buf], ks, lane), dof[ks], dp);
-        }
-        // dS packed to 16 bit. Key tiles before the diagonal and away from the ends need no
-        // mask: a uniform branch picks the mask-free form; on edge tiles every exponential is
-        // taken and masked pairs are selected to 0 (no per-element branch).
-        u32x4 dsf[2];
-        auto ds_of = [&](auto masked) {
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                float dsv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float x = fmaf(s[8 * kk + e], c2, -lse2);
-                    if constexpr (decltype(masked)::value) {
-                        const int kj = 32 * t + 16 * kk + 8 * h + e;
-                        const bool vis = qi < Nq && kj < Nk && (!p.causal || kj <= qi);
-                        x = vis ? x : -INFINITY;   // exp2(-inf) = +0
-                    }
-                    const float pe = __builtin_amdgcn_exp2f(x);
-                    dsv[e] = pe * (dp[8 * kk + e] - delta);
-                }
-                dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
-                                Mfma<T>::pack2(dsv[4], dsv[5]), Mfma<T>::pack2(dsv[6], dsv[7])};
-            }
-        };
-        const bool inner = qw0 + 32 <= Nq && 32 * t + 32 <= Nk && (!p.causal || 32 * t + 31 <= qw0);
-        if (inner) ds_of(std::false_type{});
-        else ds_of(std::true_type{});
-        // dQ^T += K^T dS^T
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int db = 0; db < TL::DB; ++db)
-                dq[db] = Mfma<T>::mma(rd_cols<D, PAD>(sK[buf], db, kk, lane), dsf[kk], dq[db]);
-        if (t + 1 < nkt) commit(buf ^ 1, other);
-        __syncthreads();
-    };
-    Stage st0, st1;
-    if (nkt > 0) {
-        fetch(0, st0);
-        commit(0, st0);
+    const int j_end = p.causal ? min(Nk, i0 + 32 * WQ) : Nk;
+    const int nkt = (j_end + KR - 1) / KR;
+
+    // this lane's chunk of a tile in each layout: slot wave * 64 + lane of the LDS image
+    // holds chunk slot % CPR of row slot / CPR, which is global chunk (slot % CPR) ^ swz(row)
+    uint32_t off_rows, off_cols;
+    {
+        const int slot = wave * 64 + lane;
+        const int row = slot / TL::CPR, pc = slot % TL::CPR;
+        const int cr = pc ^ swz<D, ROWS>(row), cc = pc ^ swz<D, COLS>(row);
+        off_rows = cr * 8 < d ? row * rs + cr * 16 : kOobOffset;
+        off_cols = cc * 8 < d ? row * rs + cc * 16 : kOobOffset;
     }
-    if (nkt > 1) fetch(1, st1);
-    __syncthreads();
-    for (int t = 0; t < nkt; t += 2) {
-        body(t, st0, st1);
-        if (t + 1 < nkt) body(t + 1, st1, st0);
+    auto lds_addr = [](const void* q) { return (uint32_t)(uintptr_t)(lds_void*)q; };
+    const int nb = Nk * (int)rs;
+    const i32x4 rk = buffer_desc(static_cast<const T*>(p.k) + kv_off, nb);
+    const i32x4 rv = buffer_desc(static_cast<const T*>(p.v) + kv_off, nb);
+    auto issue = [&](int t, int buf) {
+        const uint32_t slot = (uint32_t)wave * 1024u;
+#pragma unroll
+        for (int hf = 0; hf < KH; ++hf) {
+            const uint32_t base = (uint32_t)(KR * t + 32 * hf) * rs;
+            lds_copy16(rk, off_rows + base, __builtin_amdgcn_readfirstlane(lds_addr(sK[buf][hf]) + slot));
+            lds_copy16(rk, off_cols + base, __builtin_amdgcn_readfirstlane(lds_addr(sKc[buf][hf]) + slot));
+            lds_copy16(rv, off_rows + base, __builtin_amdgcn_readfirstlane(lds_addr(sV[buf][hf]) + slot));
+        }
+    };
+    auto body = [&](int t, int buf) {
+        // tile t landed everywhere (the copies of tile t + 1 may still be in flight when
+        // triple-buffered) and every wave is past tile t - 1, whose buffer takes the next copy
+        if (NBUF > 2 && t + 1 < nkt) {
+            constexpr int n = NCOPY * (NBUF - 2);
+            __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));   // vmcnt(n) lgkmcnt(0)
+        } else {
+            __builtin_amdgcn_s_waitcnt(7 << 4);                                   // vmcnt(0) lgkmcnt(0)
+        }
+        asm volatile("s_barrier" ::: "memory");
+        if (t + NBUF - 1 < nkt) issue(t + NBUF - 1, (buf + NBUF - 1) % NBUF);
+#pragma unroll
+        for (int hf = 0; hf < KH; ++hf) {
+            const int k0 = KR * t + 32 * hf;
+            // wave-uniform: the half holds no key this wave's rows see
+            if (k0 >= Nk || (p.causal && k0 > qw0 + 31)) continue;
+            // S^T = K Q^T, dP^T = V dO^T: register r holds key k0 + 16(r/8) + 8h + r%8, query qi
+            f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < TL::KS; ++ks) {
+                s = Mfma<T>::mma(rd_rows<D>(sK[buf][hf], ks, lane), qf[ks], s);
+                dp = Mfma<T>::mma(rd_rows<D>(sV[buf][hf], ks, lane), dof[ks], dp);
+            }
+            // dS packed to 16 bit. Halves before the diagonal and away from the ends need no
+            // mask: a uniform branch picks the mask-free form; on edge halves every exponential
+            // is taken and masked pairs are selected to 0 (no per-element branch).
+            u32x4 dsf[2];
+            auto ds_of = [&](auto masked) {
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    float dsv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        float x = fmaf(s[8 * kk + e], c2, -lse2);
+                        if constexpr (decltype(masked)::value) {
+                            const int kj = k0 + 16 * kk + 8 * h + e;
+                            const bool vis = qi < Nq && kj < Nk && (!p.causal || kj <= qi);
+                            x = vis ? x : -INFINITY;   // exp2(-inf) = +0
+                        }
+                        dsv[e] = __builtin_amdgcn_exp2f(x) * (dp[8 * kk + e] - delta);
+                    }
+                    dsf[kk] = u32x4{Mfma<T>::pack2(dsv[0], dsv[1]), Mfma<T>::pack2(dsv[2], dsv[3]),
+                                    Mfma<T>::pack2(dsv[4], dsv[5]), Mfma<T>::pack2(dsv[6], dsv[7])};
+                }
+            };
+            const bool inner = qw0 + 32 <= Nq && k0 + 32 <= Nk && (!p.causal || k0 + 31 <= qw0);
+            if (inner) ds_of(std::false_type{});
+            else ds_of(std::true_type{});
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int db = 0; db < TL::DB; ++db)
+                    dq[db] = Mfma<T>::mma(rd_cols<D>(sKc[buf][hf], db, kk, lane), dsf[kk], dq[db]);
+        }
+    };
+#pragma unroll
+    for (int t = 0; t < NBUF - 1; ++t)
+        if (t < nkt) issue(t, t);
+    for (int t = 0; t < nkt; t += NBUF) {
+#pragma unroll
+        for (int c = 0; c < NBUF; ++c)
+            if (t + c < nkt) body(t + c, c);
     }
     if (qi < Nq) store_rowT<T, D>(static_cast<T*>(p.dq) + q_off + (int64_t)qi * d, dq, p.scale, d, h);
+#endif
 }
 
 template <typename T, int D>
 hipError_t launch_typed(const BwdProblem& p, hipStream_t stream) {
-    constexpr int R = 32 * kWaves;
-    // 256 keys per dK / dV workgroup at head_dim 128 (a 32-row tile of 16-byte chunks then
-    // splits evenly over 512 threads), 128 at 64
+    // 8 waves per workgroup at head_dim 128 (a 32-row tile of 16-byte chunks then splits
+    // evenly over 512 threads), 4 at 64: 32 keys (dK / dV) or query rows (dQ) per wave
     constexpr int WV = D == 128 ? 8 : 4;
-    constexpr int RK = 32 * WV;
+    constexpr int RK = 32 * WV, R = 32 * WV;
     const int64_t nk = (int64_t)((p.seqlen_k + RK - 1) / RK) * p.heads_kv * p.batch;
     const int64_t nq = (int64_t)((p.seqlen_q + R - 1) / R) * p.heads_q * p.batch;
     if (nk > INT32_MAX || nq > INT32_MAX) return hipErrorInvalidConfiguration;
@@ -554,14 +541,14 @@ hipError_t launch_typed(const BwdProblem& p, hipStream_t stream) {
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     dim3 gk((unsigned)nk);
-    hipLaunchKernelGGL((attn_bwd_kv_mfma_kernel<T, D, 0, WV, kDvTiles, kDvBuf>), gk, dim3(WV * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_kv_mfma_kernel<T, D, 0, WV, kTiles, kBufs>), gk, dim3(WV * 64), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((attn_bwd_kv_mfma_kernel<T, D, 1, WV, kDkTiles, kDkBuf>), gk, dim3(WV * 64), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_kv_mfma_kernel<T, D, 1, WV, kTiles, kBufs>), gk, dim3(WV * 64), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess || p.seqlen_q == 0) return e;   // no query rows: dK = dV = 0, no dQ
     dim3 gq((unsigned)nq);
-    hipLaunchKernelGGL((attn_bwd_dq_mfma_kernel<T, D>), gq, dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((attn_bwd_dq_mfma_kernel<T, D, WV, kTiles, kBufs>), gq, dim3(WV * 64), 0, stream, p);
     return hipGetLastError();
 }
 
