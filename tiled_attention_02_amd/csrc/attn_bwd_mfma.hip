@@ -194,22 +194,41 @@ void attn_bwd_kv_mfma_kernel(BwdProblem p) {
     const int h = lane >> 5;
     const int Nq = p.seqlen_q, Nk = p.seqlen_k, d = p.head_dim, G = p.group;
     const uint32_t rs = (uint32_t)(d * (int)sizeof(T));
-    // flat grid, key blocks slowest: under causal masking block 0 walks every query tile and
-    // later blocks fewer, so the longest workgroups start first; the key blocks of one
-    // (batch, kv head) are heads_kv * batch apart, which keeps them on one XCD when that
-    // count is a multiple of 8 (they read the same Q and dO tiles)
-    const int per_kb = p.heads_kv * p.batch;
-    const int kb = blockIdx.x / per_kb, rem = blockIdx.x - kb * per_kb;
-    const int hk = rem % p.heads_kv, b = rem / p.heads_kv;
+    // (key block, group) of this workgroup; group = (batch, kv head). Workgroups go to the 8
+    // XCDs round-robin (blockIdx % 8). At head_dim 128 (one workgroup per CU) with S groups'
+    // key blocks filling an XCD's 32 CUs exactly, each XCD takes whole groups, S at a time,
+    // their key blocks interleaved and longest first (under causal masking block 0 walks
+    // every query tile, later blocks fewer). The first set's blocks start together and walk
+    // the query tiles from the last one down, all on the same tile; the next set's blocks
+    // start one by one as the short blocks free their CUs, longest first, so every CU ends at
+    // about the same time, and walk upwards from their first key, which puts them too on one
+    // common tile at any moment (block k starts when the front reaches its first tile). Each
+    // Q / dO tile is then read from HBM about once per set. Otherwise key blocks slowest,
+    // groups fastest, every walk downwards.
+    const int ng = p.heads_kv * p.batch, nkb = (int)(gridDim.x / (unsigned)ng);
+    const int S = D == 128 && nkb <= 32 ? 32 / nkb : 0;
+    int kb, grp;
+    bool up = false;
+    if (ng % 8 == 0 && S > 0 && S * nkb == 32 && (ng / 8) % S == 0) {
+        const int x = blockIdx.x % 8, idx = blockIdx.x / 8;
+        const int set = idx / 32, r = idx - set * 32;
+        kb = r / S;
+        grp = x + 8 * (set * S + (r - kb * S));
+        up = (set & 1) != 0;
+    } else {
+        kb = blockIdx.x / ng;
+        grp = blockIdx.x - kb * ng;
+    }
+    const int hk = grp % p.heads_kv, b = grp / p.heads_kv;
     const int j0 = kb * 32 * WV;
     const int key = j0 + 32 * wave + (lane & 31);   // this lane's key (B-operand column)
     const int64_t kv_off = ((int64_t)b * p.heads_kv + hk) * Nk * d;
-    // work: (QR-row query tile, query head g of the group), causal from the first key on.
-    // The tiles are walked from the last one down, the group's heads inner, so that the
-    // workgroups of one (batch, kv head) — which run on one XCD, whatever their first key —
-    // read the same Q / dO tile at the same time and share it through that XCD's L2. With no
-    // query rows (nit == 0) only the zero gradients are written: q, k, v, o, do and lse may
-    // then be null and are not read.
+    // work: (QR-row query tile, query head g of the group), causal from the first key on,
+    // the group's heads inner, the tiles in the direction chosen above, so that the
+    // workgroups of one (batch, kv head), which run on one XCD, read the same Q / dO tile at
+    // about the same time and share it through that XCD's L2. With no query rows (nit == 0)
+    // only the zero gradients are written: q, k, v, o, do and lse may then be null and are
+    // not read.
     const int i_start = p.causal ? j0 : 0;
     const int ntile = Nq > i_start ? (Nq - i_start + QR - 1) / QR : 0;
     const int nit = G * ntile;
@@ -238,7 +257,7 @@ void attn_bwd_kv_mfma_kernel(BwdProblem p) {
     auto lds_addr = [](const void* q) { return (uint32_t)(uintptr_t)(lds_void*)q; };
     auto tile_of = [&](int it, int& i0, int64_t& bh) {
         const int tr = it / G, g = it - tr * G;
-        i0 = i_start + QR * (ntile - 1 - tr);
+        i0 = i_start + QR * (up ? tr : ntile - 1 - tr);
         bh = (int64_t)b * p.heads_q + (int64_t)hk * G + g;
     };
     auto issue = [&](int it, int buf) {
