@@ -211,6 +211,24 @@ def test_bwd_b1_shape_groups():
             assert e <= GTOL["bf16"], f"{name} relative err {e} (b={b}, hk={hk})"
 
 
+def test_bwd_grouped_walk_noncausal():
+    """Non-causal bf16 at head_dim 128 with 32 (batch, kv head) groups of 16 key blocks
+    (B4 Hq8 Hkv8 N4096): the dK / dV passes give each XCD two groups at a time, the second
+    pair walking the query tiles upwards. Every gradient element of one group from the first
+    pair (b=0, kv head 3) and one from the second (b=3, kv head 5) against the oracle."""
+    B, Hq, Hkv, N, d = 4, 8, 8, 4096, 128
+    (q, k, v, do, sc), (o, lse, dq, dk, dv) = run(B, Hq, Hkv, N, N, d, "bf16", False, seed=21)
+    for b, hk in ((0, 3), (3, 5)):
+        rdq, rdk, rdv = oracle.attention_ref_bwd(q[b:b + 1, hk:hk + 1], k[b:b + 1, hk:hk + 1],
+                                                 v[b:b + 1, hk:hk + 1], do[b:b + 1, hk:hk + 1],
+                                                 causal=False, scale=sc)
+        errs = {"dq": rel_err(dq[b:b + 1, hk:hk + 1], rdq), "dk": rel_err(dk[b:b + 1, hk:hk + 1], rdk),
+                "dv": rel_err(dv[b:b + 1, hk:hk + 1], rdv)}
+        print(f"  b={b} hk={hk} errors {errs}", flush=True)
+        for name, e in errs.items():
+            assert e <= GTOL["bf16"], f"{name} relative err {e} (b={b}, hk={hk})"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_autograd_sum_backward(dtype):
     """flash_attention recorded for autograd: out.sum().backward() (dO = 1) fills q.grad,
