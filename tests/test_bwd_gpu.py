@@ -255,6 +255,31 @@ def test_bwd_deterministic_and_fully_written(B, Hq, Hkv, N, d, dtype, causal):
         assert torch.equal(a, b), f"{name} differs between calls"
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bwd_guard_regions_untouched(dtype):
+    """Each gradient buffer sits inside a larger allocation with 256 guard elements on each
+    side: the backward (the D pre-pass writes into dq's rows) touches none of them, and the
+    gradients equal those written into plain buffers."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 333, 128
+    print(f"bwd guards {dtype}", flush=True)
+    q, k, v = dense_inputs(B, Hq, Hkv, N, N, d, seed=61, dtype=dtype)
+    do = output_grad(q.shape, seed=61, dtype=dtype)
+    tq, tk, tv, tdo = dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(do, dtype)
+    o, lse = aule.flash_attention(tq, tk, tv, causal=True, return_lse=True)
+    ref = aule.flash_attention_backward(tq, tk, tv, o, tdo, lse, causal=True)
+    G = 256
+    bufs, views = [], []
+    for t in (tq, tk, tv):
+        big = torch.full((t.numel() + 2 * G,), 7.0, dtype=t.dtype, device=t.device)
+        bufs.append(big)
+        views.append(big[G:G + t.numel()].view(t.shape))
+    aule.flash_attention_backward(tq, tk, tv, o, tdo, lse, causal=True, grads=tuple(views))
+    torch.cuda.synchronize()
+    for name, big, view, r in zip(("dq", "dk", "dv"), bufs, views, ref):
+        assert bool((big[:G] == 7.0).all()) and bool((big[-G:] == 7.0).all()), f"{name} guard touched"
+        assert torch.equal(view, r), f"{name} differs from the plain-buffer call"
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_autograd_sum_backward(dtype):
     """flash_attention recorded for autograd: out.sum().backward() (dO = 1) fills q.grad,
